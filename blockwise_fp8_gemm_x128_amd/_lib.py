@@ -1,0 +1,57 @@
+"""ctypes loader for libpuro.so. The library must have been built (see build.py); there is no
+fallback of any kind: a missing or unloadable library raises."""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+from .build import LIB_PATH
+
+_lock = threading.Lock()
+_lib = None
+
+# Every symbol declared in include/puro.h, with its ctypes signature.
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+SIGNATURES = {
+    "puro_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "puro_abi_version": ([], ctypes.c_int),
+    "puro_quant_act_1x128": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "puro_quant_w_128x128": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "puro_quant_transpose": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "puro_fp8_gemm_fwd": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "puro_fp8_gemm_dgrad": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
+    "puro_fp8_gemm_wgrad": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P],
+                            ctypes.c_int),
+}
+
+
+class PuroError(RuntimeError):
+    """A libpuro call returned a nonzero status (or the library is unavailable)."""
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise PuroError(
+                    "libpuro.so is not built (%s); run `python -m "
+                    "blockwise_fp8_gemm_x128_amd.build`" % LIB_PATH)
+            try:  # make torch's HIP runtime the one libpuro binds to (one runtime per process)
+                import torch  # noqa: F401
+            except ImportError:  # pragma: no cover
+                pass
+            L = ctypes.CDLL(LIB_PATH)
+            for name, (args, res) in SIGNATURES.items():
+                fn = getattr(L, name)
+                fn.argtypes = args
+                fn.restype = res
+            _lib = L
+    return _lib
+
+
+def check(status: int) -> None:
+    if status != 0:
+        raise PuroError(lib().puro_status_string(status).decode())

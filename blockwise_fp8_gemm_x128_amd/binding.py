@@ -1,0 +1,128 @@
+"""Python binding of libpuro's C ABI: same names, argument marshalling only.
+
+Each function takes torch tensors that live on a HIP device, checks dtype / shape / contiguity
+/ device, allocates missing outputs with torch (device memory is PyTorch's job here), and calls
+the C entry point with raw device pointers on the current torch stream. Every step of the
+computation runs in libpuro's HIP kernels; there is no other code path.
+"""
+from __future__ import annotations
+
+import torch
+
+from ._lib import PuroError, check, lib
+
+FP8 = torch.uint8  # E4M3 codes travel as raw bytes
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape, dev) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise PuroError(f"{name}: expected a torch.Tensor")
+    if t.dtype != dtype:
+        raise PuroError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise PuroError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise PuroError(f"{name}: must be contiguous")
+    if t.device != dev:
+        raise PuroError(f"{name}: on {t.device}, expected {dev}")
+
+
+def _dev(t: torch.Tensor) -> torch.device:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise PuroError("inputs must be torch tensors on a HIP device")
+    return t.device
+
+
+def _out(t, name, dtype, shape, dev):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=dev)
+    _need(t, name, dtype, shape, dev)
+    return t
+
+
+def puro_quant_act_1x128(x: torch.Tensor, q=None, s=None):
+    """x bf16 [rows, cols] -> (q uint8 E4M3 [rows, cols], s fp32 [cols/128, rows])."""
+    dev = _dev(x)
+    rows, cols = x.shape
+    _need(x, "x", torch.bfloat16, (rows, cols), dev)
+    q = _out(q, "q", FP8, (rows, cols), dev)
+    s = _out(s, "s", torch.float32, (cols // 128, rows), dev)
+    check(lib().puro_quant_act_1x128(x.data_ptr(), rows, cols, q.data_ptr(), s.data_ptr(),
+                                     _stream(dev)))
+    return q, s
+
+
+def puro_quant_w_128x128(w: torch.Tensor, q=None, s=None):
+    """w bf16 [n, k] -> (q uint8 E4M3 [n, k], s fp32 [n/128, k/128])."""
+    dev = _dev(w)
+    n, k = w.shape
+    _need(w, "w", torch.bfloat16, (n, k), dev)
+    q = _out(q, "q", FP8, (n, k), dev)
+    s = _out(s, "s", torch.float32, (n // 128, k // 128), dev)
+    check(lib().puro_quant_w_128x128(w.data_ptr(), n, k, q.data_ptr(), s.data_ptr(),
+                                     _stream(dev)))
+    return q, s
+
+
+def puro_quant_transpose(x: torch.Tensor, qt=None, st=None):
+    """x bf16 [rows, cols] -> (qt uint8 E4M3 [cols, rows], st fp32 [rows/128, cols])."""
+    dev = _dev(x)
+    rows, cols = x.shape
+    _need(x, "x", torch.bfloat16, (rows, cols), dev)
+    qt = _out(qt, "qt", FP8, (cols, rows), dev)
+    st = _out(st, "st", torch.float32, (rows // 128, cols), dev)
+    check(lib().puro_quant_transpose(x.data_ptr(), rows, cols, qt.data_ptr(), st.data_ptr(),
+                                     _stream(dev)))
+    return qt, st
+
+
+def puro_fp8_gemm_fwd(xq, sx, wq, sw, y=None):
+    """Y bf16 [M, N] from xq [M, K], sx [K/128, M], wq [N, K], sw [N/128, K/128]."""
+    dev = _dev(xq)
+    M, K = xq.shape
+    N = wq.shape[0]
+    _need(xq, "xq", FP8, (M, K), dev)
+    _need(sx, "sx", torch.float32, (K // 128, M), dev)
+    _need(wq, "wq", FP8, (N, K), dev)
+    _need(sw, "sw", torch.float32, (N // 128, K // 128), dev)
+    y = _out(y, "y", torch.bfloat16, (M, N), dev)
+    check(lib().puro_fp8_gemm_fwd(xq.data_ptr(), sx.data_ptr(), wq.data_ptr(), sw.data_ptr(),
+                                  y.data_ptr(), M, N, K, _stream(dev)))
+    return y
+
+
+def puro_fp8_gemm_dgrad(dyq, sdy, wq, sw, dx=None):
+    """dX bf16 [M, K] from dyq [M, N], sdy [N/128, M], wq [N, K], sw [N/128, K/128]."""
+    dev = _dev(dyq)
+    M, N = dyq.shape
+    K = wq.shape[1]
+    _need(dyq, "dyq", FP8, (M, N), dev)
+    _need(sdy, "sdy", torch.float32, (N // 128, M), dev)
+    _need(wq, "wq", FP8, (N, K), dev)
+    _need(sw, "sw", torch.float32, (N // 128, K // 128), dev)
+    dx = _out(dx, "dx", torch.bfloat16, (M, K), dev)
+    check(lib().puro_fp8_gemm_dgrad(dyq.data_ptr(), sdy.data_ptr(), wq.data_ptr(),
+                                    sw.data_ptr(), dx.data_ptr(), M, N, K, _stream(dev)))
+    return dx
+
+
+def puro_fp8_gemm_wgrad(dytq, sdyt, xtq, sxt, dw=None, accumulate: bool = False):
+    """dW fp32 [N, K] (= or +=) from dytq [N, M], sdyt [M/128, N], xtq [K, M], sxt [M/128, K]."""
+    dev = _dev(dytq)
+    N, M = dytq.shape
+    K = xtq.shape[0]
+    _need(dytq, "dytq", FP8, (N, M), dev)
+    _need(sdyt, "sdyt", torch.float32, (M // 128, N), dev)
+    _need(xtq, "xtq", FP8, (K, M), dev)
+    _need(sxt, "sxt", torch.float32, (M // 128, K), dev)
+    if accumulate and dw is None:
+        raise PuroError("accumulate=True needs an existing dw")
+    dw = _out(dw, "dw", torch.float32, (N, K), dev)
+    check(lib().puro_fp8_gemm_wgrad(dytq.data_ptr(), sdyt.data_ptr(), xtq.data_ptr(),
+                                    sxt.data_ptr(), dw.data_ptr(), M, N, K,
+                                    1 if accumulate else 0, _stream(dev)))
+    return dw

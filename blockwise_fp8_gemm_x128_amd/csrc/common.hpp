@@ -1,0 +1,74 @@
+// Shared host validation and device helpers for libpuro (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "puro.h"
+
+namespace puro {
+
+// ---------------------------------------------------------------- host-side validation
+constexpr int64_t kGroup = 128;
+// Largest accepted dimension; keeps every element offset far inside int64 and every grid
+// inside hipLaunchKernel's 32-bit limits.
+constexpr int64_t kMaxDim = int64_t(1) << 24;
+
+inline bool dim_ok(int64_t d) { return d >= 0 && d <= kMaxDim && d % kGroup == 0; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks one tensor pointer: NULL is only accepted for an empty tensor.
+inline puro_status check_ptr(const void* p, bool empty) {
+  if (empty) return PURO_OK;
+  if (p == nullptr) return PURO_ERR_NULL;
+  if (!aligned16(p)) return PURO_ERR_ALIGN;
+  return PURO_OK;
+}
+
+inline puro_status launch_status() {
+  return hipGetLastError() == hipSuccess ? PURO_OK : PURO_ERR_LAUNCH;
+}
+
+#define PURO_TRY(expr)                   \
+  do {                                   \
+    puro_status st_ = (expr);            \
+    if (st_ != PURO_OK) return st_;      \
+  } while (0)
+
+// ---------------------------------------------------------------- device helpers
+// bf16 <-> fp32: bf16 is the high half of a binary32, so widening is a shift.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Four fp32 values, already multiplied by the group's reciprocal scale, to four OCP E4M3 bytes
+// (byte i holds value i). The clamp to +-448 is the contract's saturation step; the convert
+// rounds to nearest even and keeps the sign of zero.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
+  d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+  return static_cast<uint32_t>(v);
+}
+
+// Scale and reciprocal of a group from its max magnitude: s = amax/448, r = 448/amax, each a
+// single correctly rounded fp32 division; an all-zero group gets s = r = 1.
+__device__ __forceinline__ void group_scale(float amax, float& s, float& r) {
+  if (amax == 0.0f) {
+    s = 1.0f;
+    r = 1.0f;
+  } else {
+    s = amax / 448.0f;
+    r = 448.0f / amax;
+  }
+}
+
+}  // namespace puro

@@ -1,0 +1,240 @@
+// Blockwise FP8 quantisers for gfx950: 1x128 row groups, 128x128 weight blocks, and the
+// transposed 1x128 requantisation used by the weight-gradient GEMM.
+//
+// Method: Paper walkthrough: Puro-2B (ta-paperlens.web.app), section "Lever 2: use blockwise
+// FP8 from step zero" — scales are taken per local group, activations and their gradients in
+// groups of 128 along the reduction dimension and weights in 128x128 blocks. Number formats
+// and rounding as stated in include/puro.h.
+//
+// All three kernels are HBM-bound: each bf16 element is read once (2 B) and its E4M3 code
+// written once (1 B), plus one fp32 scale per group. Loads are 16 B per lane and every wave
+// instruction touches whole 128 B (or larger) segments; all per-element arithmetic (widen,
+// |max|, multiply, clamp, packed convert) stays in registers.
+#include "common.hpp"
+
+namespace puro {
+namespace {
+
+// ------------------------------------------------------------------ 1x128 row groups
+// One group = 128 consecutive bf16 of a row = 16 lanes x 8 elements. A 256-thread block holds
+// 16 groups per pass and makes 4 passes, so it covers 64 consecutive rows of one 128-column
+// chunk. Blocks walk the chunks of a row band first so neighbouring blocks read neighbouring
+// 256 B segments of the same rows.
+constexpr int kActPasses = 4;
+constexpr int kActRowsPerBlock = 16 * kActPasses;
+
+__global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t* __restrict__ x,
+                                                              int64_t rows, int64_t cols,
+                                                              uint8_t* __restrict__ q,
+                                                              float* __restrict__ s) {
+  const int64_t chunks = cols >> 7;
+  const int64_t c = blockIdx.x % chunks;
+  const int64_t rb = blockIdx.x / chunks;
+  const int seg = threadIdx.x >> 4;
+  const int l16 = threadIdx.x & 15;
+
+  uint4 v[kActPasses];
+#pragma unroll
+  for (int p = 0; p < kActPasses; ++p) {
+    const int64_t row = rb * kActRowsPerBlock + p * 16 + seg;
+    v[p] = *reinterpret_cast<const uint4*>(x + row * cols + c * 128 + l16 * 8);
+  }
+#pragma unroll
+  for (int p = 0; p < kActPasses; ++p) {
+    const int64_t row = rb * kActRowsPerBlock + p * 16 + seg;
+    float f[8] = {bf16_lo(v[p].x), bf16_hi(v[p].x), bf16_lo(v[p].y), bf16_hi(v[p].y),
+                  bf16_lo(v[p].z), bf16_hi(v[p].z), bf16_lo(v[p].w), bf16_hi(v[p].w)};
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, __builtin_fabsf(f[i]));
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
+    float sc, r;
+    group_scale(m, sc, r);
+    uint2 out;
+    out.x = e4m3x4(f[0] * r, f[1] * r, f[2] * r, f[3] * r);
+    out.y = e4m3x4(f[4] * r, f[5] * r, f[6] * r, f[7] * r);
+    *reinterpret_cast<uint2*>(q + row * cols + c * 128 + l16 * 8) = out;
+    if (l16 == 0) s[c * rows + row] = sc;
+  }
+}
+
+// ------------------------------------------------------------------ 128x128 weight blocks
+// One 256-thread block per 128x128 block: 16 lanes cover a 256 B row, 8 passes of 16 rows.
+__global__ __launch_bounds__(256) void quant_w_128x128_kernel(const uint16_t* __restrict__ w,
+                                                              int64_t n, int64_t k,
+                                                              uint8_t* __restrict__ q,
+                                                              float* __restrict__ s) {
+  __shared__ float wave_max[4];
+  const int64_t kblocks = k >> 7;
+  const int64_t bj = blockIdx.x % kblocks;
+  const int64_t bi = blockIdx.x / kblocks;
+  const int t = threadIdx.x;
+  const int r0 = t >> 4;
+  const int col = (t & 15) * 8;
+
+  uint4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t row = bi * 128 + r0 + 16 * i;
+    v[i] = *reinterpret_cast<const uint4*>(w + row * k + bj * 128 + col);
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    m = fmaxf(m, __builtin_fabsf(bf16_lo(v[i].x)));
+    m = fmaxf(m, __builtin_fabsf(bf16_hi(v[i].x)));
+    m = fmaxf(m, __builtin_fabsf(bf16_lo(v[i].y)));
+    m = fmaxf(m, __builtin_fabsf(bf16_hi(v[i].y)));
+    m = fmaxf(m, __builtin_fabsf(bf16_lo(v[i].z)));
+    m = fmaxf(m, __builtin_fabsf(bf16_hi(v[i].z)));
+    m = fmaxf(m, __builtin_fabsf(bf16_lo(v[i].w)));
+    m = fmaxf(m, __builtin_fabsf(bf16_hi(v[i].w)));
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if ((t & 63) == 0) wave_max[t >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+  float sc, r;
+  group_scale(m, sc, r);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t row = bi * 128 + r0 + 16 * i;
+    uint2 out;
+    out.x = e4m3x4(bf16_lo(v[i].x) * r, bf16_hi(v[i].x) * r, bf16_lo(v[i].y) * r,
+                   bf16_hi(v[i].y) * r);
+    out.y = e4m3x4(bf16_lo(v[i].z) * r, bf16_hi(v[i].z) * r, bf16_lo(v[i].w) * r,
+                   bf16_hi(v[i].w) * r);
+    *reinterpret_cast<uint2*>(q + row * k + bj * 128 + col) = out;
+  }
+  if (t == 0) s[bi * kblocks + bj] = sc;
+}
+
+// ------------------------------------------------------------------ transposed 1x128 groups
+// Tile = 128 rows x 64 columns of x (one group per column). Load: 8 lanes per 128 B row
+// segment, 4 passes of 32 rows, staged in LDS as dwords (2 bf16) with a 33-dword row pitch.
+// Compute: wave w owns tile columns [16w, 16w+16) as 8 column pairs; lane = 8*g + pair holds
+// rows [16g, 16g+16) of its pair, so a column's amax is an 8-lane reduction and a column's
+// 128 output bytes are written by 8 lanes as one contiguous 128 B segment.
+constexpr int kTrPitch = 33;  // dwords per staged row (32 data + 1 pad)
+
+__global__ __launch_bounds__(256) void quant_transpose_kernel(const uint16_t* __restrict__ x,
+                                                              int64_t rows, int64_t cols,
+                                                              uint8_t* __restrict__ qt,
+                                                              float* __restrict__ st) {
+  __shared__ uint32_t tile[128 * kTrPitch];
+  const int64_t cblocks = cols >> 6;
+  const int64_t cb = blockIdx.x % cblocks;
+  const int64_t mb = blockIdx.x / cblocks;
+  const int64_t m0 = mb * 128, c0 = cb * 64;
+  const int t = threadIdx.x;
+
+  {
+    const int r = t >> 3, c8 = t & 7;
+    uint4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      v[i] = *reinterpret_cast<const uint4*>(x + (m0 + r + 32 * i) * cols + c0 + c8 * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t* dst = tile + (r + 32 * i) * kTrPitch + c8 * 4;
+      dst[0] = v[i].x;
+      dst[1] = v[i].y;
+      dst[2] = v[i].z;
+      dst[3] = v[i].w;
+    }
+  }
+  __syncthreads();
+
+  const int w = t >> 6, lane = t & 63;
+  const int pair = lane & 7, g = lane >> 3;
+  const int dc = w * 8 + pair;  // dword column: tile columns 2*dc, 2*dc+1
+  uint32_t d[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) d[i] = tile[(16 * g + i) * kTrPitch + dc];
+  float m0v = 0.0f, m1v = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    m0v = fmaxf(m0v, __builtin_fabsf(bf16_lo(d[i])));
+    m1v = fmaxf(m1v, __builtin_fabsf(bf16_hi(d[i])));
+  }
+#pragma unroll
+  for (int off = 8; off < 64; off <<= 1) {
+    m0v = fmaxf(m0v, __shfl_xor(m0v, off, 64));
+    m1v = fmaxf(m1v, __shfl_xor(m1v, off, 64));
+  }
+  float s0, r0, s1, r1;
+  group_scale(m0v, s0, r0);
+  group_scale(m1v, s1, r1);
+  uint4 o0, o1;
+  o0.x = e4m3x4(bf16_lo(d[0]) * r0, bf16_lo(d[1]) * r0, bf16_lo(d[2]) * r0, bf16_lo(d[3]) * r0);
+  o0.y = e4m3x4(bf16_lo(d[4]) * r0, bf16_lo(d[5]) * r0, bf16_lo(d[6]) * r0, bf16_lo(d[7]) * r0);
+  o0.z = e4m3x4(bf16_lo(d[8]) * r0, bf16_lo(d[9]) * r0, bf16_lo(d[10]) * r0,
+                bf16_lo(d[11]) * r0);
+  o0.w = e4m3x4(bf16_lo(d[12]) * r0, bf16_lo(d[13]) * r0, bf16_lo(d[14]) * r0,
+                bf16_lo(d[15]) * r0);
+  o1.x = e4m3x4(bf16_hi(d[0]) * r1, bf16_hi(d[1]) * r1, bf16_hi(d[2]) * r1, bf16_hi(d[3]) * r1);
+  o1.y = e4m3x4(bf16_hi(d[4]) * r1, bf16_hi(d[5]) * r1, bf16_hi(d[6]) * r1, bf16_hi(d[7]) * r1);
+  o1.z = e4m3x4(bf16_hi(d[8]) * r1, bf16_hi(d[9]) * r1, bf16_hi(d[10]) * r1,
+                bf16_hi(d[11]) * r1);
+  o1.w = e4m3x4(bf16_hi(d[12]) * r1, bf16_hi(d[13]) * r1, bf16_hi(d[14]) * r1,
+                bf16_hi(d[15]) * r1);
+  const int64_t col = c0 + 2 * dc;
+  *reinterpret_cast<uint4*>(qt + col * rows + m0 + 16 * g) = o0;
+  *reinterpret_cast<uint4*>(qt + (col + 1) * rows + m0 + 16 * g) = o1;
+  if (g == 0) *reinterpret_cast<float2*>(st + mb * cols + col) = make_float2(s0, s1);
+}
+
+}  // namespace
+}  // namespace puro
+
+using namespace puro;
+
+extern "C" puro_status puro_quant_act_1x128(const void* x, int64_t rows, int64_t cols, void* q,
+                                            float* s, void* stream) {
+  if (!dim_ok(rows) || !dim_ok(cols)) return PURO_ERR_SHAPE;
+  const bool empty = rows == 0 || cols == 0;
+  PURO_TRY(check_ptr(x, empty));
+  PURO_TRY(check_ptr(q, empty));
+  PURO_TRY(check_ptr(s, empty));
+  if (empty) return PURO_OK;
+  const int64_t blocks = (rows / kActRowsPerBlock) * (cols / 128);
+  if (blocks > INT32_MAX) return PURO_ERR_SHAPE;
+  hipLaunchKernelGGL(quant_act_1x128_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(x), rows,
+                     cols, static_cast<uint8_t*>(q), s);
+  return launch_status();
+}
+
+extern "C" puro_status puro_quant_w_128x128(const void* w, int64_t n, int64_t k, void* q,
+                                            float* s, void* stream) {
+  if (!dim_ok(n) || !dim_ok(k)) return PURO_ERR_SHAPE;
+  const bool empty = n == 0 || k == 0;
+  PURO_TRY(check_ptr(w, empty));
+  PURO_TRY(check_ptr(q, empty));
+  PURO_TRY(check_ptr(s, empty));
+  if (empty) return PURO_OK;
+  const int64_t blocks = (n / 128) * (k / 128);
+  if (blocks > INT32_MAX) return PURO_ERR_SHAPE;
+  hipLaunchKernelGGL(quant_w_128x128_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(w), n, k,
+                     static_cast<uint8_t*>(q), s);
+  return launch_status();
+}
+
+extern "C" puro_status puro_quant_transpose(const void* x, int64_t rows, int64_t cols, void* qt,
+                                            float* st, void* stream) {
+  if (!dim_ok(rows) || !dim_ok(cols)) return PURO_ERR_SHAPE;
+  const bool empty = rows == 0 || cols == 0;
+  PURO_TRY(check_ptr(x, empty));
+  PURO_TRY(check_ptr(qt, empty));
+  PURO_TRY(check_ptr(st, empty));
+  if (empty) return PURO_OK;
+  const int64_t blocks = (rows / 128) * (cols / 64);
+  if (blocks > INT32_MAX) return PURO_ERR_SHAPE;
+  hipLaunchKernelGGL(quant_transpose_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(x), rows,
+                     cols, static_cast<uint8_t*>(qt), st);
+  return launch_status();
+}

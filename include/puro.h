@@ -1,0 +1,116 @@
+/*
+ * puro.h — C ABI of libpuro.so: blockwise-FP8 quantisers and GEMMs for the linear layers of a
+ * transformer, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (Paper walkthrough: Puro-2B, ta-paperlens.web.app, section
+ * "Lever 2: use blockwise FP8 from step zero"; PuRo-2B news post, jj-blog.pages.dev,
+ * driver-hack section, training-recipe paragraph): the linear-layer GEMMs — forward
+ * Y = X·Wᵀ, data gradient dX = dY·W and weight gradient dW = dYᵀ·X — run on FP8 operands whose
+ * scales are kept per local group: activations and activation gradients per 1x128 group along
+ * the GEMM's reduction dimension, weights per 128x128 block. Masters stay in higher precision:
+ * weights come in as bf16, Y and dX go out as bf16, dW goes out as fp32.
+ *
+ * Number formats fixed by this library where the pages are silent:
+ *   payload  OCP FP8 E4M3 ("e4m3fn": bias 7, largest finite 448, no infinities,
+ *            NaN = S.1111.111; never produced), one byte per element;
+ *   scale    fp32 s = amax/448 (one correctly rounded division) for a group with max |x| = amax;
+ *            an all-zero group has s = 1;
+ *   payload  q = E4M3_RNE(clamp(x * (448/amax), -448, 448)) with 448/amax one correctly rounded
+ *            fp32 division and the product one fp32 multiply; the sign of zero is kept;
+ *   GEMM     out = sum over 128-element reduction chunks of (s_a * s_b) * (chunk dot product),
+ *            the chunk dot product taken on matrix cores, the sum kept in fp32.
+ *
+ * Conventions for every entry point:
+ *   - All pointers are DEVICE pointers owned by the caller; the library allocates, frees and
+ *     synchronises nothing and keeps no state between calls (calls are thread-safe).
+ *   - Every tensor is dense row-major. Tensor pointers must be 16-byte aligned.
+ *   - Every dimension must be a multiple of 128 (zero allowed). A call whose output is empty
+ *     returns PURO_OK and launches nothing. A GEMM whose reduction dimension is 0 writes zeros
+ *     (or leaves dW unchanged when accumulating).
+ *   - `stream` is a hipStream_t (NULL = the default stream). Work is enqueued asynchronously;
+ *     the call returns once it is queued.
+ *   - Validation is done on the host before anything is enqueued: a failed check returns a
+ *     nonzero status and enqueues nothing. A failed launch returns PURO_ERR_LAUNCH.
+ *   - Inputs must be finite, and a nonzero group must have amax >= 2^-119 (so that 448/amax is
+ *     finite); such inputs are not checked on the device.
+ *   - Output buffers must not overlap inputs.
+ */
+#ifndef PURO_H
+#define PURO_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PURO_OK = 0,
+  PURO_ERR_NULL = 1,   /* a required pointer is NULL while its tensor is non-empty */
+  PURO_ERR_SHAPE = 2,  /* a dimension is negative, not a multiple of 128, or too large */
+  PURO_ERR_ALIGN = 3,  /* a tensor pointer is not 16-byte aligned */
+  PURO_ERR_LAUNCH = 4, /* the HIP runtime rejected a kernel launch */
+  PURO_ERR_ARG = 5     /* another argument is out of range (e.g. `accumulate` not 0/1) */
+} puro_status;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* puro_status_string(int status);
+/* Version of this ABI; bumped on any incompatible change. */
+int puro_abi_version(void);
+
+/* 1x128 quantiser for activations (forward, groups along K) and activation gradients (dgrad,
+ * groups along N): groups of 128 consecutive elements of each row.
+ *   x  bf16 [rows][cols]        (input)
+ *   q  e4m3 [rows][cols]        (output payload, same layout as x)
+ *   s  fp32 [cols/128][rows]    (output scales, chunk-major: scales of one chunk column are
+ *                                contiguous over rows) */
+puro_status puro_quant_act_1x128(const void* x, int64_t rows, int64_t cols, void* q, float* s,
+                                 void* stream);
+
+/* 128x128 block quantiser for weights; one scale serves both the forward (reduce over K) and the
+ * data-gradient GEMM (reduce over N) because the block is square.
+ *   w  bf16 [n][k]              (input, the bf16 master copy)
+ *   q  e4m3 [n][k]              (output payload)
+ *   s  fp32 [n/128][k/128]      (output block scales) */
+puro_status puro_quant_w_128x128(const void* w, int64_t n, int64_t k, void* q, float* s,
+                                 void* stream);
+
+/* Transposed 1x128 requantiser for the weight-gradient GEMM, whose reduction dimension is the
+ * token dimension: groups of 128 consecutive ROWS of each column, requantised from bf16, and
+ * written transposed so that every group is contiguous. Equals puro_quant_act_1x128 applied to
+ * the transpose of x.
+ *   x   bf16 [rows][cols]       (input, e.g. X[M][K] or dY[M][N])
+ *   qt  e4m3 [cols][rows]       (output payload, transposed)
+ *   st  fp32 [rows/128][cols]   (output scales) */
+puro_status puro_quant_transpose(const void* x, int64_t rows, int64_t cols, void* qt, float* st,
+                                 void* stream);
+
+/* Forward GEMM  Y[m][n] = sum_kb sx[kb][m] * sw[n/128][kb] * sum_{k in kb} xq[m][k] * wq[n][k].
+ *   xq e4m3 [M][K], sx fp32 [K/128][M]      (from puro_quant_act_1x128 of X)
+ *   wq e4m3 [N][K], sw fp32 [N/128][K/128]  (from puro_quant_w_128x128 of W)
+ *   y  bf16 [M][N]                           (output, round-to-nearest-even) */
+puro_status puro_fp8_gemm_fwd(const void* xq, const float* sx, const void* wq, const float* sw,
+                              void* y, int64_t M, int64_t N, int64_t K, void* stream);
+
+/* Data-gradient GEMM  dX[m][k] = sum_nb sdy[nb][m] * sw[nb][k/128] * sum_{n in nb} dyq[m][n] * wq[n][k].
+ * The weight payload and scales are the forward ones, used unchanged.
+ *   dyq e4m3 [M][N], sdy fp32 [N/128][M]    (from puro_quant_act_1x128 of dY)
+ *   wq  e4m3 [N][K], sw  fp32 [N/128][K/128]
+ *   dx  bf16 [M][K]                          (output) */
+puro_status puro_fp8_gemm_dgrad(const void* dyq, const float* sdy, const void* wq,
+                                const float* sw, void* dx, int64_t M, int64_t N, int64_t K,
+                                void* stream);
+
+/* Weight-gradient GEMM  dW[n][k] (=, or += when accumulate = 1)
+ *     sum_mb sdyt[mb][n] * sxt[mb][k] * sum_{m in mb} dytq[n][m] * xtq[k][m].
+ *   dytq e4m3 [N][M], sdyt fp32 [M/128][N]  (from puro_quant_transpose of dY[M][N])
+ *   xtq  e4m3 [K][M], sxt  fp32 [M/128][K]  (from puro_quant_transpose of X[M][K])
+ *   dw   fp32 [N][K]                         (output; read too when accumulate = 1, which lets
+ *                                             micro-batches sum into one FP32 gradient) */
+puro_status puro_fp8_gemm_wgrad(const void* dytq, const float* sdyt, const void* xtq,
+                                const float* sxt, float* dw, int64_t M, int64_t N, int64_t K,
+                                int accumulate, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PURO_H */

@@ -1,0 +1,86 @@
+"""Host-side checks of the C ABI (no GPU needed): libpuro.so loads, exports every function
+declared in include/puro.h, and its validation rejects bad arguments before touching the
+device. None of these calls reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "puro.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from blockwise_fp8_gemm_x128_amd import _lib
+    from blockwise_fp8_gemm_x128_amd.build import LIB_PATH, build
+    if not os.path.exists(LIB_PATH):
+        build(verbose=False)
+    return _lib.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(puro_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_six_entry_points():
+    names = declared_functions()
+    for n in ("puro_quant_act_1x128", "puro_quant_w_128x128", "puro_quant_transpose",
+              "puro_fp8_gemm_fwd", "puro_fp8_gemm_dgrad", "puro_fp8_gemm_wgrad"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    from blockwise_fp8_gemm_x128_amd._lib import SIGNATURES
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert name in SIGNATURES, name
+
+
+def test_version_and_status_strings(L):
+    assert L.puro_abi_version() == 1
+    assert L.puro_status_string(0) == b"PURO_OK"
+    for code in range(1, 6):
+        assert L.puro_status_string(code).startswith(b"PURO_ERR_")
+    assert L.puro_status_string(99) == b"unknown puro_status"
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation first
+MIS = 0x10001   # misaligned
+
+
+@pytest.mark.parametrize("fn", ["puro_quant_act_1x128", "puro_quant_w_128x128",
+                                "puro_quant_transpose"])
+def test_quant_validation(L, fn):
+    f = getattr(L, fn)
+    assert f(FAKE, 100, 128, FAKE, FAKE, None) == 2          # ragged rows
+    assert f(FAKE, 128, 200, FAKE, FAKE, None) == 2          # ragged cols
+    assert f(FAKE, -128, 128, FAKE, FAKE, None) == 2         # negative
+    assert f(FAKE, 1 << 25, 128, FAKE, FAKE, None) == 2      # beyond the size limit
+    assert f(None, 128, 128, FAKE, FAKE, None) == 1          # NULL input
+    assert f(FAKE, 128, 128, None, FAKE, None) == 1          # NULL payload
+    assert f(FAKE, 128, 128, FAKE, None, None) == 1          # NULL scales
+    assert f(MIS, 128, 128, FAKE, FAKE, None) == 3           # misaligned
+    assert f(FAKE, 128, 128, FAKE, MIS, None) == 3
+    assert f(None, 0, 128, None, None, None) == 0            # empty: nothing to do
+    assert f(None, 256, 0, None, None, None) == 0
+
+
+def test_gemm_validation(L):
+    fwd, dgrad, wgrad = L.puro_fp8_gemm_fwd, L.puro_fp8_gemm_dgrad, L.puro_fp8_gemm_wgrad
+    for f in (fwd, dgrad):
+        assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 130, 128, 128, None) == 2
+        assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 128, 128, 64, None) == 2
+        assert f(None, FAKE, FAKE, FAKE, FAKE, 128, 128, 128, None) == 1
+        assert f(FAKE, FAKE, FAKE, FAKE, None, 128, 128, 128, None) == 1
+        assert f(FAKE, FAKE, MIS, FAKE, FAKE, 128, 128, 128, None) == 3
+        assert f(None, None, None, None, None, 0, 128, 128, None) == 0
+    assert fwd(None, None, None, None, None, 128, 0, 128, None) == 0
+    assert dgrad(None, None, None, None, None, 128, 128, 0, None) == 0
+    assert wgrad(FAKE, FAKE, FAKE, FAKE, FAKE, 128, 128, 128, 2, None) == 5
+    assert wgrad(FAKE, FAKE, FAKE, FAKE, FAKE, 128, 96, 128, 0, None) == 2
+    assert wgrad(FAKE, FAKE, FAKE, FAKE, None, 128, 128, 128, 0, None) == 1
+    assert wgrad(None, None, None, None, None, 128, 0, 128, 1, None) == 0

@@ -1,0 +1,195 @@
+"""GPU parity of the three GEMMs against the oracle, element by element, under the acceptance
+rule |gpu - oracle| <= 2^-7 |oracle| + 1e-3 rms(oracle). The oracle quantises the same bf16
+inputs itself (its quantised operands are bit-identical to the GPU's, which the quantiser
+tests check separately) and computes exact chunk products with double accumulation.
+
+Small shapes are compared in full; the full-size layer shapes (M = 4096, 8192, 16384) on
+seeded samples of output rows (all columns), which the oracle computes one row at a time."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from blockwise_fp8_gemm_x128_amd import synth
+from helpers import bf16_np, gemm_tolerance_violations
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def bf16_to_np64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def sample_rows(total, n, seed):
+    if n >= total:
+        return np.arange(total)
+    rng = np.random.default_rng(seed)
+    pick = rng.choice(np.arange(1, total - 1), size=n - 2, replace=False)
+    return np.sort(np.concatenate([[0, total - 1], pick]))
+
+
+def check(gpu, ref, what):
+    nbad, worst = gemm_tolerance_violations(gpu, ref)
+    assert nbad == 0, f"{what}: {nbad} elements out of tolerance (worst err/bound {worst:.3g})"
+    return worst
+
+
+def run_fwd(puro, oracle, x, w, rows=None, what="fwd"):
+    M, K = x.shape
+    N = w.shape[0]
+    say(what, "fwd M,N,K =", M, N, K)
+    xq, sx = puro.puro_quant_act_1x128(x.cuda())
+    wq, sw = puro.puro_quant_w_128x128(w.cuda())
+    y = puro.puro_fp8_gemm_fwd(xq, sx, wq, sw)
+    torch.cuda.synchronize()
+    oxq, osx = oracle.quant_act_1x128(bf16_np(x))
+    owq, osw = oracle.quant_w_128x128(bf16_np(w))
+    ref = oracle.gemm_fwd(oxq, osx, owq, osw, rows=rows)
+    got = bf16_to_np64(y if rows is None else y[torch.as_tensor(rows).cuda()])
+    return check(got, ref, what)
+
+
+def run_dgrad(puro, oracle, dy, w, rows=None, what="dgrad"):
+    M, N = dy.shape
+    K = w.shape[1]
+    say(what, "dgrad M,N,K =", M, N, K)
+    dyq, sdy = puro.puro_quant_act_1x128(dy.cuda())
+    wq, sw = puro.puro_quant_w_128x128(w.cuda())
+    dx = puro.puro_fp8_gemm_dgrad(dyq, sdy, wq, sw)
+    torch.cuda.synchronize()
+    odyq, osdy = oracle.quant_act_1x128(bf16_np(dy))
+    owq, osw = oracle.quant_w_128x128(bf16_np(w))
+    ref = oracle.gemm_dgrad(odyq, osdy, owq, osw, rows=rows)
+    got = bf16_to_np64(dx if rows is None else dx[torch.as_tensor(rows).cuda()])
+    return check(got, ref, what)
+
+
+def run_wgrad(puro, oracle, dy, x, rows=None, what="wgrad", dw0=None):
+    M, N = dy.shape
+    K = x.shape[1]
+    say(what, "wgrad M,N,K =", M, N, K)
+    dytq, sdyt = puro.puro_quant_transpose(dy.cuda())
+    xtq, sxt = puro.puro_quant_transpose(x.cuda())
+    dw_in = None if dw0 is None else dw0.clone().cuda()
+    dw = puro.puro_fp8_gemm_wgrad(dytq, sdyt, xtq, sxt, dw=dw_in, accumulate=dw0 is not None)
+    torch.cuda.synchronize()
+    odytq, osdyt = oracle.quant_transpose(bf16_np(dy))
+    oxtq, osxt = oracle.quant_transpose(bf16_np(x))
+    ref = oracle.gemm_wgrad(odytq, osdyt, oxtq, osxt, rows=rows)
+    if dw0 is not None:
+        base = dw0.numpy().astype(np.float64)
+        ref = ref + (base if rows is None else base[rows])
+    got = dw.cpu().numpy().astype(np.float64)
+    if rows is not None:
+        got = got[rows]
+    return check(got, ref, what)
+
+
+def test_tiny_forward(puro, oracle):
+    x, w = synth.tiny_forward_inputs()
+    run_fwd(puro, oracle, x, w, what="tiny 256^3")
+
+
+SMALL = [(128, 128, 128), (384, 640, 384), (256, 384, 1152), (640, 256, 256), (1024, 768, 512)]
+
+
+@pytest.mark.parametrize("M,N,K", SMALL)
+def test_small_all_three(puro, oracle, M, N, K):
+    seed = M * 7 + N * 3 + K
+    x = synth.randn_bf16((M, K), 1.0, seed)
+    w = synth.randn_bf16((N, K), 0.02, seed + 1)
+    dy = synth.randn_bf16((M, N), 1e-3, seed + 2)
+    run_fwd(puro, oracle, x, w, what=f"fwd {M}x{N}x{K}")
+    run_dgrad(puro, oracle, dy, w, what=f"dgrad {M}x{N}x{K}")
+    run_wgrad(puro, oracle, dy, x, what=f"wgrad {M}x{N}x{K}")
+
+
+def test_wgrad_accumulate(puro, oracle):
+    M, N, K = 512, 256, 384
+    x = synth.randn_bf16((M, K), 1.0, 71)
+    dy = synth.randn_bf16((M, N), 1e-3, 72)
+    dw0 = torch.randn((N, K), generator=torch.Generator().manual_seed(73)) * 1e-2
+    run_wgrad(puro, oracle, dy, x, dw0=dw0, what="wgrad accumulate")
+
+
+def test_zero_reduction(puro):
+    say("zero reduction")
+    xq = torch.empty((256, 0), dtype=torch.uint8, device="cuda")
+    sx = torch.empty((0, 256), dtype=torch.float32, device="cuda")
+    wq = torch.empty((384, 0), dtype=torch.uint8, device="cuda")
+    sw = torch.empty((3, 0), dtype=torch.float32, device="cuda")
+    y = torch.full((256, 384), 7.0, dtype=torch.bfloat16, device="cuda")
+    puro.puro_fp8_gemm_fwd(xq, sx, wq, sw, y=y)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y).item() == 0
+    # wgrad with M = 0: overwrite gives zeros, accumulate leaves dW unchanged
+    dytq = torch.empty((256, 0), dtype=torch.uint8, device="cuda")
+    sdyt = torch.empty((0, 256), dtype=torch.float32, device="cuda")
+    xtq = torch.empty((128, 0), dtype=torch.uint8, device="cuda")
+    sxt = torch.empty((0, 128), dtype=torch.float32, device="cuda")
+    dw = torch.full((256, 128), 3.0, dtype=torch.float32, device="cuda")
+    puro.puro_fp8_gemm_wgrad(dytq, sdyt, xtq, sxt, dw=dw, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.all(dw == 3.0)
+    puro.puro_fp8_gemm_wgrad(dytq, sdyt, xtq, sxt, dw=dw, accumulate=False)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dw).item() == 0
+
+
+def test_zero_groups_and_scale_isolation(puro, oracle):
+    # rows with all-zero 1x128 tiles and one outlier block: exercises the s = 1 path inside GEMMs
+    M, N, K = 384, 256, 512
+    x = synth.randn_bf16((M, K), 1.0, 81).float()
+    x[5, 128:256] = 0
+    x[100:228, 384:] = 0
+    x[7, :] *= 1000.0
+    x = x.to(torch.bfloat16)
+    w = synth.randn_bf16((N, K), 0.02, 82).float()
+    w[128:, 256:384] *= 50.0
+    w = w.to(torch.bfloat16)
+    run_fwd(puro, oracle, x, w, what="fwd zero/outlier")
+
+
+def test_deterministic(puro):
+    M, N, K = 512, 512, 1024
+    x = synth.randn_bf16((M, K), 1.0, 91).cuda()
+    w = synth.randn_bf16((N, K), 0.02, 92).cuda()
+    xq, sx = puro.puro_quant_act_1x128(x)
+    wq, sw = puro.puro_quant_w_128x128(w)
+    y1 = puro.puro_fp8_gemm_fwd(xq, sx, wq, sw)
+    y2 = puro.puro_fp8_gemm_fwd(xq, sx, wq, sw)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("li", range(4))
+def test_layer_forward_m4096(puro, oracle, li):
+    name, K, N = synth.LINEARS[li]
+    x, w, _ = synth.linear_inputs(1, li, 4096, K, N)
+    run_fwd(puro, oracle, x, w, rows=sample_rows(4096, 48, li), what=f"{name} fwd M=4096")
+
+
+@pytest.mark.parametrize("M", [8192, 16384])
+@pytest.mark.parametrize("li", range(4))
+def test_layer_fwd_bwd(puro, oracle, M, li):
+    name, K, N = synth.LINEARS[li]
+    config = 2 if M == 16384 else 4
+    x, w, dy = synth.linear_inputs(config, li, M, K, N)
+    run_fwd(puro, oracle, x, w, rows=sample_rows(M, 24, li), what=f"{name} fwd M={M}")
+    run_dgrad(puro, oracle, dy, w, rows=sample_rows(M, 24, li + 10), what=f"{name} dgrad M={M}")
+    run_wgrad(puro, oracle, dy, x, rows=sample_rows(N, 16, li + 20), what=f"{name} wgrad M={M}")
+
+
+def test_outlier_fwd_bwd(puro, oracle):
+    x, w, dy, _ = synth.outlier_inputs()
+    M, K = x.shape
+    N = w.shape[0]
+    run_fwd(puro, oracle, x, w, rows=sample_rows(M, 32, 1), what="outlier fwd")
+    run_dgrad(puro, oracle, dy, w, rows=sample_rows(M, 32, 2), what="outlier dgrad")
+    run_wgrad(puro, oracle, dy, x, rows=sample_rows(N, 16, 3), what="outlier wgrad")

@@ -1,0 +1,140 @@
+"""GPU parity of the three quantisers: payload bytes and scales must equal the oracle's bit for
+bit, on the tiny configuration, multi-tile and ragged shapes, special values, every bf16 value
+of the representable range, and the full-size Qwen3-1.7B layer shapes (M = 4096 and 16384) and
+the outlier stress inputs."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from blockwise_fp8_gemm_x128_amd import synth
+from helpers import bf16_np
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_act(puro, x):
+    q, s = puro.puro_quant_act_1x128(x.cuda())
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy()
+
+
+def gpu_w(puro, w):
+    q, s = puro.puro_quant_w_128x128(w.cuda())
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy()
+
+
+def gpu_tr(puro, x):
+    q, s = puro.puro_quant_transpose(x.cuda())
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy()
+
+
+def assert_same(gq, gs, oq, os_, what):
+    assert gq.shape == oq.shape and gs.shape == os_.shape, what
+    bad = np.argwhere(gq != oq)
+    assert bad.size == 0, f"{what}: {len(bad)} payload mismatches, first {bad[:5].tolist()}"
+    badv = np.argwhere(gs.view(np.uint32) != os_.view(np.uint32))
+    assert badv.size == 0, f"{what}: {len(badv)} scale mismatches, first {badv[:5].tolist()}"
+
+
+def check_all_three(puro, oracle, x, what, weight=True, transpose=True):
+    say("quant", what, tuple(x.shape))
+    xn = bf16_np(x)
+    gq, gs = gpu_act(puro, x)
+    oq, os_ = oracle.quant_act_1x128(xn)
+    assert_same(gq, gs, oq, os_, what + " act")
+    if weight:
+        gq, gs = gpu_w(puro, x)
+        oq, os_ = oracle.quant_w_128x128(xn)
+        assert_same(gq, gs, oq, os_, what + " w")
+    if transpose:
+        gq, gs = gpu_tr(puro, x)
+        oq, os_ = oracle.quant_transpose(xn)
+        assert_same(gq, gs, oq, os_, what + " transpose")
+
+
+def test_tiny_config(puro, oracle):
+    x, w = synth.tiny_forward_inputs()
+    check_all_three(puro, oracle, x, "tiny X")
+    check_all_three(puro, oracle, w, "tiny W")
+
+
+@pytest.mark.parametrize("shape,std,seed", [
+    ((128, 128), 1.0, 101), ((384, 640), 0.02, 102), ((256, 6144), 1e-3, 103),
+    ((640, 128), 7.0, 104), ((1152, 384), 1e-30, 105)])
+def test_shapes(puro, oracle, shape, std, seed):
+    x = synth.randn_bf16(shape, std, seed)
+    check_all_three(puro, oracle, x, f"randn std={std}")
+
+
+def test_special_values(puro, oracle):
+    rows = []
+    z = np.zeros(128, np.float32)
+    rows.append(z.copy())                                     # all +0
+    r = z.copy(); r[::2] = -0.0; rows.append(r)               # mixed signed zeros
+    r = z.copy(); r[3] = -1.0; rows.append(r)                 # one nonzero among zeros
+    r = z.copy(); r[0] = 2.0 ** -118; r[1] = 2.0 ** -127; r[2] = -(2.0 ** -130)
+    r[3] = 2.0 ** -133; r[4] = -(2.0 ** -121); rows.append(r)  # small amax, bf16 subnormals
+    r = np.full(128, 3.0e38, np.float32); r[::3] *= -1; rows.append(r)              # huge
+    r = np.linspace(-448, 448, 128).astype(np.float32); rows.append(r)
+    r = (2.0 ** np.arange(-64, 64)).astype(np.float32); rows.append(r)              # wide range
+    r = np.full(128, 1.0, np.float32); r[5] = 1.0e-8; r[6] = -2.0e-7; rows.append(r)  # underflow
+    x = torch.tensor(np.stack(rows)).to(torch.bfloat16)
+    pad = torch.zeros((128 - x.shape[0], 128), dtype=torch.bfloat16)
+    x = torch.cat([x, pad])
+    check_all_three(puro, oracle, x, "special")
+
+
+def test_every_bf16_value_through_unit_scale(puro, oracle):
+    # groups of 127 bf16 values plus one 448: scale 1, so every representable-range bf16 value
+    # reaches the E4M3 rounding unchanged (covers ties, subnormals, signed zeros)
+    bits = np.arange(65536, dtype=np.uint32)
+    vals = (bits << 16).view(np.float32)
+    vals = vals[np.isfinite(vals) & (np.abs(vals) <= 448.0)]
+    n = len(vals)
+    rows = (n + 126) // 127
+    rows = (rows + 127) // 128 * 128
+    grid = np.zeros((rows, 128), np.float32)
+    flat = np.zeros(rows * 127, np.float32)
+    flat[:n] = vals
+    grid[:, :127] = flat.reshape(rows, 127)
+    grid[:, 127] = 448.0
+    x = torch.tensor(grid).to(torch.bfloat16)
+    check_all_three(puro, oracle, x, "all bf16", weight=False, transpose=False)
+
+
+@pytest.mark.parametrize("M", [4096, 16384])
+@pytest.mark.parametrize("li", range(4))
+def test_layer_shapes(puro, oracle, M, li):
+    name, K, N = synth.LINEARS[li]
+    config = 1 if M == 4096 else 2
+    x, w, dy = synth.linear_inputs(config, li, M, K, N)
+    check_all_three(puro, oracle, x, f"{name} X M={M}", weight=False, transpose=(M == 16384))
+    if M == 4096:
+        check_all_three(puro, oracle, w, f"{name} W", weight=True, transpose=False)
+    else:
+        check_all_three(puro, oracle, dy, f"{name} dY M={M}", weight=False, transpose=True)
+
+
+def test_outlier_stress(puro, oracle):
+    x, w, dy, picks = synth.outlier_inputs()
+    check_all_three(puro, oracle, x, "outlier X", weight=False, transpose=True)
+    check_all_three(puro, oracle, w, "outlier W", weight=True, transpose=False)
+    # the zeroed tiles quantise to scale 1 and zero codes
+    q, s = gpu_act(puro, x)
+    rows, tcols = picks["zero_tiles"]
+    assert np.all(s[tcols.numpy(), rows.numpy()] == 1.0)
+
+
+def test_empty(puro):
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    q, s = puro.puro_quant_act_1x128(x)
+    assert q.shape == (0, 256) and s.shape == (2, 0)

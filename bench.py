@@ -1,0 +1,282 @@
+"""Benchmark: one training step of the blockwise-FP8 linear stack of a Qwen3-1.7B-shaped model.
+
+A step = 28 layers x 4 linear GEMM groups (qkv 2048->4096, o 2048->2048, gate_up 2048->12288,
+down 6144->2048) at M = 8192 tokens (2 sequences of 4096):
+  forward  (layer 0..27, qkv..down): quant_w_128x128(W), quant_act_1x128(X), fp8_gemm_fwd
+  backward (layer 27..0, down..qkv): quant_act_1x128(dY), fp8_gemm_dgrad,
+                                     quant_transpose(dY), quant_transpose(X), fp8_gemm_wgrad
+Every layer has its own seeded bf16 X, W, dY and fp32 dW buffers resident in HBM (~26 GB), so
+the 256 MB last-level cache cannot serve one layer's data to the next.
+
+Prints one JSON line: whole-step tokens/s, per-kernel times from HIP events recorded around
+every launch on the launch stream inside the timed region, the dominant kernel's roofline
+fraction, and the CPU oracle timed on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("blockwise-FP8 GEMM TFLOP/s (% of FP8 peak); quant GB/s; linear-stack tokens/s")
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+M_TOKENS = 8192
+
+# algorithmic bytes per element of the quantisers: 2 B bf16 read + 1 B E4M3 write + scale share
+B_ACT = 2 + 1 + 4 / 128
+B_W = 2 + 1 + 4 / (128 * 128)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--layers", type=int, default=28, help=argparse.SUPPRESS)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-kernel-events", action="store_true",
+                   help="time the step without per-kernel events")
+    return p.parse_args()
+
+
+class Stack:
+    """Device buffers and pre-marshalled launches of the whole step."""
+
+    def __init__(self, layers: int, M: int):
+        import torch
+        from blockwise_fp8_gemm_x128_amd import binding as B
+        from blockwise_fp8_gemm_x128_amd import synth
+
+        dev = torch.device("cuda:0")
+        self.launches = []  # (kernel class, flops, bytes, callable)
+        shared = {}
+
+        def buf(key, shape, dtype):
+            if key not in shared:
+                shared[key] = torch.empty(shape, dtype=dtype, device=dev)
+            return shared[key]
+
+        self.persist = []
+        fwd, bwd = [], []
+        for layer in range(layers):
+            for li, (name, K, N) in enumerate(synth.LINEARS):
+                s = lambda kind: synth.stack_seed(layer, li, kind)  # noqa: E731
+                x = synth.randn_bf16((M, K), synth.X_STD, s(synth.KIND_X), dev)
+                w = synth.randn_bf16((N, K), synth.W_STD, s(synth.KIND_W), dev)
+                dy = synth.randn_bf16((M, N), synth.DY_STD, s(synth.KIND_DY), dev)
+                wq = torch.empty((N, K), dtype=torch.uint8, device=dev)
+                sw = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
+                dw = torch.empty((N, K), dtype=torch.float32, device=dev)
+                xq = buf(("xq", M, K), (M, K), torch.uint8)
+                sx = buf(("sx", M, K), (K // 128, M), torch.float32)
+                y = buf(("y", M, N), (M, N), torch.bfloat16)
+                dyq = buf(("dyq", M, N), (M, N), torch.uint8)
+                sdy = buf(("sdy", M, N), (N // 128, M), torch.float32)
+                dx = buf(("dx", M, K), (M, K), torch.bfloat16)
+                dytq = buf(("dytq", M, N), (N, M), torch.uint8)
+                sdyt = buf(("sdyt", M, N), (M // 128, N), torch.float32)
+                xtq = buf(("xtq", M, K), (K, M), torch.uint8)
+                sxt = buf(("sxt", M, K), (M // 128, K), torch.float32)
+                self.persist += [x, w, dy, wq, sw, dw]
+                f = 2.0 * M * N * K
+                fwd += [
+                    ("quant_w_128x128", 0.0, N * K * B_W,
+                     B.prepare("puro_quant_w_128x128", w, N, K, wq, sw)),
+                    ("quant_act_1x128", 0.0, M * K * B_ACT,
+                     B.prepare("puro_quant_act_1x128", x, M, K, xq, sx)),
+                    ("gemm_fwd", f, 0.0,
+                     B.prepare("puro_fp8_gemm_fwd", xq, sx, wq, sw, y, M, N, K)),
+                ]
+                bwd.append([
+                    ("quant_act_1x128", 0.0, M * N * B_ACT,
+                     B.prepare("puro_quant_act_1x128", dy, M, N, dyq, sdy)),
+                    ("gemm_dgrad", f, 0.0,
+                     B.prepare("puro_fp8_gemm_dgrad", dyq, sdy, wq, sw, dx, M, N, K)),
+                    ("quant_transpose", 0.0, M * N * B_ACT,
+                     B.prepare("puro_quant_transpose", dy, M, N, dytq, sdyt)),
+                    ("quant_transpose", 0.0, M * K * B_ACT,
+                     B.prepare("puro_quant_transpose", x, M, K, xtq, sxt)),
+                    ("gemm_wgrad", f, 0.0,
+                     B.prepare("puro_fp8_gemm_wgrad", dytq, sdyt, xtq, sxt, dw, M, N, K, 0)),
+                ])
+        self.launches = fwd + [op for grp in reversed(bwd) for op in grp]
+        self.flops = sum(l[1] for l in self.launches)
+        self.bytes = sum(l[2] for l in self.launches)
+
+    def run(self, events=None):
+        if events is None:
+            for _, _, _, call in self.launches:
+                call()
+        else:
+            for (_, _, _, call), (e0, e1) in zip(self.launches, events):
+                e0.record()
+                call()
+                e1.record()
+
+
+def cpu_baseline(M: int, layers: int, rows_fwd: int = 64, rows_wgrad: int = 8):
+    """The oracle on the host cores, on a bounded sample of one step: every quantiser of one
+    layer at full size, and each GEMM of that layer on a seeded sample of output rows (all
+    columns), extrapolated linearly to all rows and then to all layers."""
+    import numpy as np
+
+    import oracle
+    from blockwise_fp8_gemm_x128_amd import synth
+
+    def u16(t):
+        return t.contiguous().view(__import__("torch").int16).numpy().view(np.uint16)
+
+    t_quant = t_gemm = 0.0
+    rng = np.random.default_rng(0)
+    for li, (name, K, N) in enumerate(synth.LINEARS):
+        x = u16(synth.randn_bf16((M, K), synth.X_STD, synth.stack_seed(0, li, synth.KIND_X)))
+        w = u16(synth.randn_bf16((N, K), synth.W_STD, synth.stack_seed(0, li, synth.KIND_W)))
+        dy = u16(synth.randn_bf16((M, N), synth.DY_STD, synth.stack_seed(0, li, synth.KIND_DY)))
+        t0 = time.perf_counter()
+        wq, sw = oracle.quant_w_128x128(w)
+        xq, sx = oracle.quant_act_1x128(x)
+        dyq, sdy = oracle.quant_act_1x128(dy)
+        dytq, sdyt = oracle.quant_transpose(dy)
+        xtq, sxt = oracle.quant_transpose(x)
+        t1 = time.perf_counter()
+        t_quant += t1 - t0
+        rf = np.sort(rng.choice(M, rows_fwd, replace=False))
+        rw = np.sort(rng.choice(N, rows_wgrad, replace=False))
+        t0 = time.perf_counter()
+        oracle.gemm_fwd(xq, sx, wq, sw, rows=rf)
+        t1 = time.perf_counter()
+        oracle.gemm_dgrad(dyq, sdy, wq, sw, rows=rf)
+        t2 = time.perf_counter()
+        oracle.gemm_wgrad(dytq, sdyt, xtq, sxt, rows=rw)
+        t3 = time.perf_counter()
+        t_gemm += (t1 - t0) * M / rows_fwd + (t2 - t1) * M / rows_fwd + (t3 - t2) * N / rows_wgrad
+    step_s = layers * (t_quant + t_gemm)
+    return {
+        "value": M / step_s,
+        "unit": "tokens/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"layer 0 of the step: all 5 quantiser passes per linear at full size "
+                   f"(timed), each GEMM on {rows_fwd} sampled output rows (fwd, dgrad) or "
+                   f"{rows_wgrad} rows (wgrad) of all columns, extrapolated linearly to all rows "
+                   f"and x{layers} layers"),
+        "step_s_extrapolated": step_s,
+        "quant_s_per_layer": t_quant,
+        "gemm_s_per_layer_extrapolated": t_gemm,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(multi-GPU runs are out of scope: the path shards by data parallelism, see the "
+              "design notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    M = M_TOKENS
+    stack = Stack(args.layers, M)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        stack.run()
+    torch.cuda.synchronize()
+
+    use_events = not args.no_kernel_events
+    ev_sets = []
+    if use_events:
+        for _ in range(args.steps):
+            ev_sets.append([(torch.cuda.Event(enable_timing=True),
+                             torch.cuda.Event(enable_timing=True)) for _ in stack.launches])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        stack.run(ev_sets[k] if use_events else None)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    per_class = {}
+    if use_events:
+        for evs in ev_sets:
+            for (cls, fl, by, _), (e0, e1) in zip(stack.launches, evs):
+                d = per_class.setdefault(cls, {"ms": 0.0, "launches": 0, "flops": 0.0,
+                                               "bytes": 0.0})
+                d["ms"] += e0.elapsed_time(e1)
+                d["launches"] += 1
+                d["flops"] += fl
+                d["bytes"] += by
+    kernels = {}
+    for cls, d in per_class.items():
+        n = args.steps
+        ent = {"ms_per_step": d["ms"] / n, "launches_per_step": d["launches"] // n,
+               "avg_launch_us": 1e3 * d["ms"] / d["launches"]}
+        if d["flops"]:
+            tf = d["flops"] / (d["ms"] * 1e-3) / 1e12
+            ent.update({"tflops": tf, "frac_fp8_peak": tf / PEAK_FP8_TFLOPS})
+        else:
+            gb = d["bytes"] / (d["ms"] * 1e-3) / 1e9
+            ent.update({"gbps": gb, "frac_hbm_peak": gb / PEAK_HBM_GBPS})
+        kernels[cls] = ent
+    roofline = None
+    if kernels:
+        dom = max(kernels, key=lambda c: kernels[c]["ms_per_step"])
+        k = kernels[dom]
+        if "tflops" in k:
+            roofline = {"bound": "mfma", "achieved": k["tflops"], "peak": PEAK_FP8_TFLOPS,
+                        "unit": "TFLOP/s", "frac": k["frac_fp8_peak"], "traffic": None,
+                        "kernel": dom}
+        else:
+            roofline = {"bound": "hbm", "achieved": k["gbps"], "peak": PEAK_HBM_GBPS,
+                        "unit": "GB/s", "frac": k["frac_hbm_peak"], "traffic": None,
+                        "kernel": dom}
+    gemm_ms = sum(v["ms_per_step"] for c, v in kernels.items() if c.startswith("gemm"))
+    quant_ms = sum(v["ms_per_step"] for c, v in kernels.items() if c.startswith("quant"))
+    gemm_flops = sum(l[1] for l in stack.launches)
+    quant_bytes = sum(l[2] for l in stack.launches)
+    roof_ms = (gemm_flops / (PEAK_FP8_TFLOPS * 1e12) + quant_bytes / (PEAK_HBM_GBPS * 1e9)) * 1e3
+
+    out = {
+        "metric": METRIC,
+        "value": M / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic (seeded N(0,1) X, N(0,0.02^2) W, N(0,1e-3^2) dY, bf16)",
+        "config": {"workload": "Qwen3-1.7B-shaped linear stack step: 28 layers x "
+                               "{qkv 2048->4096, o 2048->2048, gate_up 2048->12288, "
+                               "down 6144->2048}, fwd + dgrad + wgrad + all quantisers",
+                   "tokens_per_step": M, "seqs": M // 4096, "seq_len": 4096,
+                   "layers": args.layers, "parallelism": "single GPU"},
+        "gemm_tflops": gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None,
+        "gemm_frac_fp8_peak": (gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS
+                               if gemm_ms else None),
+        "quant_gbps": quant_bytes / (quant_ms * 1e-3) / 1e9 if quant_ms else None,
+        "quant_frac_hbm_peak": (quant_bytes / (quant_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS
+                                if quant_ms else None),
+        "roofline_step_ms": roof_ms,
+        "step_frac_of_roofline": roof_ms / ms_per_step,
+        "kernel_event_sum_ms_per_step": gemm_ms + quant_ms,
+        "kernels": kernels,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(M, args.layers)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

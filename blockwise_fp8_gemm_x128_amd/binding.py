@@ -126,3 +126,27 @@ def puro_fp8_gemm_wgrad(dytq, sdyt, xtq, sxt, dw=None, accumulate: bool = False)
                                     sxt.data_ptr(), dw.data_ptr(), M, N, K,
                                     1 if accumulate else 0, _stream(dev)))
     return dw
+
+
+def prepare(name: str, *args):
+    """Pre-marshalled call of a C entry point for hot loops: tensors become raw device
+    pointers, the current torch stream is bound, and the returned zero-argument callable
+    only crosses into the C ABI (which still validates) and checks the status."""
+    fn = getattr(lib(), name)
+    dev = None
+    conv = []
+    for a in args:
+        if isinstance(a, torch.Tensor):
+            dev = dev or a.device
+            conv.append(a.data_ptr())
+        else:
+            conv.append(a)
+    stream = _stream(dev)
+    conv.append(stream)
+
+    def call():
+        st = fn(*conv)
+        if st != 0:
+            check(st)
+
+    return call

@@ -19,9 +19,13 @@
 // a WM x WN sub-tile = (WM/16) x (WN/16) MFMA tiles of 16x16. The reduction runs in 128-wide
 // chunks through a two-stage LDS pipeline: while chunk c is multiplied out of one stage, chunk
 // c+1 (A tile, B tile and the A/B scale rows) streams into the other stage with
-// global_load_lds_dwordx4, which writes LDS directly (no VGPR staging, no ds_write). One barrier
-// per chunk separates "stage landed" from "stage free". Each 128-byte row of a staged operand
-// keeps its 16-byte pieces XOR-permuted so fragment reads spread over the LDS banks.
+// buffer_load_dwordx4 ... lds, which writes LDS directly (no VGPR staging, no ds_write). One
+// barrier per chunk separates "stage landed" from "stage free". Each 128-byte row of a staged
+// operand keeps its eight 16-byte pieces XOR-permuted (piece p at slot p ^ swz(row)). gfx950
+// serves a 16-byte-per-lane LDS read 32 lanes at a time over a 512-byte bank window, and an
+// 8-byte transposed read 64 lanes at a time; the two swizzles below make the MFMA fragment
+// reads (16 rows x 2 lane groups per pass) and the transposed reads (4 lane groups x 8 rows x
+// 2 halves) hit distinct bank slots.
 //
 // Block order: workgroups are dispatched round-robin over the 8 XCDs, so the block id is first
 // remapped so that consecutive tiles run on one XCD (sharing that XCD's L2), and tiles are
@@ -36,7 +40,13 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+// LDS pointers keep their address space from the kernel entry down, so no generic-to-LDS
+// conversions (with their null checks) appear inside the pipeline.
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) v2i lds_v2i;
+typedef __attribute__((address_space(3))) v4i lds_v4i_t;
+typedef __attribute__((address_space(3))) v4f lds_v4f;
+typedef __attribute__((address_space(3))) float lds_f32;
 typedef __attribute__((address_space(3))) void lds_void;
 
 enum Mode : int { kFwd = 0, kDgrad = 1, kWgrad = 2 };
@@ -68,12 +78,15 @@ struct Cfg {
   static_assert(WM <= 128 && 128 % WM == 0, "a wave's rows lie in one 128-row half");
   static_assert((BM / 8) % kWaves == 0 && (BN / 8) % kWaves == 0, "even DMA split");
   static_assert(BM / 4 <= 64 && BN / 4 <= 64, "one DMA instruction per scale row");
-  static_assert(WM % 64 == 0 || WM == 16 * MI, "row-block swizzle parity is per-block");
   static_assert(!kBTrans || WN == 64, "reduction-major B fragment offsets assume WN = 64");
 };
 
-// Row r of a staged 128-byte-row array keeps its eight 16-byte pieces in XOR-permuted order.
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ ((row >> 5) << 2)) & 7; }
+// Swizzle of row-major staged operands (A, and B of forward / wgrad): row bits 2 and 3 -> slot
+// bits 0 and 2 (bit 1 is left to the lane group of the fragment read).
+__device__ __forceinline__ int swz_rows(int row) { return ((row >> 2) & 1) | ((row >> 1) & 4); }
+// Swizzle of reduction-major slabs (B of dgrad): row bit 2 -> slot bit 0, row bits 5-6 -> slot
+// bits 1-2.
+__device__ __forceinline__ int swz_slab(int row) { return ((row >> 2) & 1) | ((row >> 4) & 6); }
 
 __device__ __forceinline__ int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
 
@@ -95,7 +108,7 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
                                            kRsrcWord3);
 }
 
-__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* lds_dst) {
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, lds_u8* lds_dst) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 16, static_cast<int>(voff),
                                            static_cast<int>(soff), 0, 0);
 }
@@ -106,9 +119,11 @@ struct Loader {
   static constexpr int kBInstr = C::BN / 8 / C::kWaves;  // and B tile
 
   // Instruction k of wave w copies staged rows [8q, 8q+8), q = w + kWaves*k; lane l takes row
-  // 8q + l/8 and physical piece l%8, i.e. logical piece (l%8) ^ swz(row). That XOR term does not
-  // depend on k, so all of a lane's instructions share one per-lane offset; the row offset of
-  // instruction k and the chunk offset are wave-uniform (scalar offset / resource base).
+  // 8q + l/8 and physical piece l%8, i.e. logical piece (l%8) ^ swz(row). For row-major operands
+  // swz_rows(8q + l/8) depends only on l and on q & 1 = w & 1 (kWaves is even), so all of a
+  // lane's instructions share one per-lane offset; for slabs swz_slab depends on k as well and
+  // each instruction gets its own. Row and chunk offsets are wave-uniform (scalar offset or
+  // resource base).
   const uint8_t* A;
   const uint8_t* B;
   const float* sA;
@@ -116,17 +131,23 @@ struct Loader {
   int64_t I, J, L, i0, j0;
   rsrc_t ra, rb;          // per-tile resources (A, and row-major B)
   uint32_t a_voff, b_voff;
+  uint32_t bt_voff[kBInstr];  // reduction-major B: per instruction
   int wave, lane;
   const float* sb_block;  // block modes: the wave's block scale of chunk 0 (uniform)
   int64_t sb_block_step;
 
   __device__ __forceinline__ void init(int wn) {
+    static_assert(C::kWaves % 2 == 0, "row-major DMA swizzle assumes an even wave count");
     const int r8 = lane >> 3, p8 = lane & 7;
-    const int xr = ((8 * wave + r8) >> 1 ^ ((8 * wave + r8) >> 5) << 2) & 7;  // swz, any k
+    const int xr = swz_rows(8 * wave + r8);  // = swz_rows(8q + r8) for every instruction k
     ra = make_rsrc(A + i0 * L, (I - i0) * L);
     a_voff = static_cast<uint32_t>(r8 * L + ((p8 ^ xr) << 4));
     if (C::kBTrans) {
-      b_voff = static_cast<uint32_t>(r8 * J + ((p8 ^ xr) << 4));
+#pragma unroll
+      for (int k = 0; k < kBInstr; ++k) {
+        const int rr = 8 * ((wave + C::kWaves * k) & 15) + r8;  // row inside its slab
+        bt_voff[k] = static_cast<uint32_t>(r8 * J + ((p8 ^ swz_slab(rr)) << 4));
+      }
     } else {
       rb = make_rsrc(B + j0 * L, (J - j0) * L);
       b_voff = static_cast<uint32_t>(r8 * L + ((p8 ^ xr) << 4));
@@ -143,7 +164,7 @@ struct Loader {
   }
 
   // Enqueue chunk c into `stage` (every wave issues its share; DMA writes LDS directly).
-  __device__ __forceinline__ void issue(uint8_t* stage, int64_t c) const {
+  __device__ __forceinline__ void issue(lds_u8* stage, int64_t c) const {
 #pragma unroll
     for (int k = 0; k < kAInstr; ++k) {
       const int q = wave + C::kWaves * k;
@@ -159,7 +180,7 @@ struct Loader {
       for (int k = 0; k < kBInstr; ++k) {
         const int q = wave + C::kWaves * k;
         const int sl = q >> 4, qq = q & 15;
-        dma16(rbc, b_voff, static_cast<uint32_t>(8 * qq * J + 128 * sl),
+        dma16(rbc, bt_voff[k], static_cast<uint32_t>(8 * qq * J + 128 * sl),
               stage + C::kBOff + 8 * q * kChunk);
       }
     } else {
@@ -177,77 +198,73 @@ struct Loader {
   }
 };
 
-// Per-lane LDS byte offsets of this wave's fragment reads, fixed for the whole kernel.
-// For 16 consecutive staged rows R0 + r (R0 a multiple of 16) the swizzle is
-// swz(R0 + r) = ((r >> 1) & 7) ^ 4 * ((R0 >> 5) & 1): a per-lane term and a term known per row
-// block, so two variants (f = 0 / 4) cover every row block of the wave.
+// Per-lane LDS byte offsets of this wave's fragment reads, fixed for the whole kernel. Every
+// row-major fragment covers 16 staged rows starting at a multiple of 16, so its swizzle term
+// swz_rows(R0 + r) = swz_rows(r) depends on the lane only; every transposed read of lane
+// 16G + r touches slab row 32G + 8i + r/2, whose swz_slab term is (r >> 3) | 2G for all i.
 template <class C>
 struct FragOffsets {
-  int a[2][2];      // [f/4][half]: A rows, wave-relative
-  int b[2][2];      // same for row-major B
-  int bt[2][4];     // reduction-major B: [i & 1][nj]
-  int sa;           // this lane's 4 A scales (wave-relative)
-  int sb;           // this lane's B scale column base (per-column mode)
+  int a[2];    // [half]: A rows, wave-relative
+  int b[2];    // same for row-major B
+  int bt[4];   // reduction-major B, per nj
+  int sa;      // this lane's 4 A scales (wave-relative)
+  int sb;      // this lane's B scale column base (per-column mode)
 
   __device__ __forceinline__ void init(int wm, int wn, int lane) {
     const int G = lane >> 4, r = lane & 15;
-    for (int f = 0; f < 2; ++f)
-      for (int e = 0; e < 2; ++e) {
-        const int x = ((2 * G + e) ^ ((r >> 1) & 7) ^ (4 * f)) << 4;
-        a[f][e] = C::kAOff + (wm * C::WM + r) * kChunk + x;
-        b[f][e] = C::kBOff + (wn * C::WN + r) * kChunk + x;
-      }
+    for (int e = 0; e < 2; ++e) {
+      const int x = ((2 * G + e) ^ swz_rows(r)) << 4;
+      a[e] = C::kAOff + (wm * C::WM + r) * kChunk + x;
+      b[e] = C::kBOff + (wn * C::WN + r) * kChunk + x;
+    }
     // Reduction-major B (dgrad): fragment (nj, i) reads slab (col >> 7), row 32G + 8i + r/2,
-    // piece (col & 127) >> 4 = 4 * (wn & 1) + nj when WN = 64, swizzled by
-    // swz(row) = (4i & 7) ^ (r >> 2) ^ 4 * (G & 1).
-    const int y = (r >> 2) ^ (4 * ((G & 1) ^ ((wn * C::WN >> 6) & 1)));
+    // 8 bytes at 8 * (r & 1) of piece (col & 127) >> 4, where col = wn * WN + 16 nj.
     const int slab = ((wn * C::WN) >> 7) * kSlab;
-    for (int io = 0; io < 2; ++io)
-      for (int nj = 0; nj < 4; ++nj)
-        bt[io][nj] = C::kBOff + slab + (32 * G + (r >> 1)) * kChunk + 8 * (r & 1) +
-                     ((nj ^ y ^ (4 * io)) << 4);
+    const int xs = swz_slab(32 * G + (r >> 1));
+    for (int nj = 0; nj < 4; ++nj) {
+      const int piece = (((wn * C::WN) & 127) >> 4) + nj;
+      bt[nj] = C::kBOff + slab + (32 * G + (r >> 1)) * kChunk + 8 * (r & 1) + ((piece ^ xs) << 4);
+    }
     sa = C::kSAOff + (wm * C::WM + 4 * G) * 4;
     sb = C::kSBOff + (wn * C::WN + r) * 4;
   }
 };
 
 template <int kOff>
-__device__ __forceinline__ v4i lds_v4i(const uint8_t* stage, int off) {
-  return *reinterpret_cast<const v4i*>(stage + off + kOff);
+__device__ __forceinline__ v4i lds_v4i(const lds_u8* stage, int off) {
+  return *reinterpret_cast<const lds_v4i_t*>(stage + off + kOff);
 }
 
 // A-type fragment: 16 rows starting at wave row 16*mi.
 template <class C, int mi>
-__device__ __forceinline__ v8i frag_a(const uint8_t* stage, const FragOffsets<C>& o) {
-  constexpr int f = (mi >> 1) & 1;  // (16 mi >> 5) & 1; the wave's row origin is a multiple of 64
-  const v4i lo = lds_v4i<16 * mi * kChunk>(stage, o.a[f][0]);
-  const v4i hi = lds_v4i<16 * mi * kChunk>(stage, o.a[f][1]);
+__device__ __forceinline__ v8i frag_a(const lds_u8* stage, const FragOffsets<C>& o) {
+  const v4i lo = lds_v4i<16 * mi * kChunk>(stage, o.a[0]);
+  const v4i hi = lds_v4i<16 * mi * kChunk>(stage, o.a[1]);
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 template <class C, int nj>
-__device__ __forceinline__ v8i frag_b(const uint8_t* stage, const FragOffsets<C>& o) {
+__device__ __forceinline__ v8i frag_b(const lds_u8* stage, const FragOffsets<C>& o) {
   if (C::kBTrans) {
     v8i f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const v2i v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-          (lds_v2i*)(stage + o.bt[i & 1][nj] + 8 * i * kChunk));
+          (lds_v2i*)(stage + o.bt[nj] + 8 * i * kChunk));
       f[2 * i] = v[0];
       f[2 * i + 1] = v[1];
     }
     return f;
   } else {
-    constexpr int f = (nj >> 1) & 1;
-    const v4i lo = lds_v4i<16 * nj * kChunk>(stage, o.b[f][0]);
-    const v4i hi = lds_v4i<16 * nj * kChunk>(stage, o.b[f][1]);
+    const v4i lo = lds_v4i<16 * nj * kChunk>(stage, o.b[0]);
+    const v4i hi = lds_v4i<16 * nj * kChunk>(stage, o.b[1]);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
 }
 
 template <class C, int mi>
-__device__ __forceinline__ v4f scale_a(const uint8_t* stage, const FragOffsets<C>& o) {
-  return *reinterpret_cast<const v4f*>(stage + o.sa + 16 * mi * 4);
+__device__ __forceinline__ v4f scale_a(const lds_u8* stage, const FragOffsets<C>& o) {
+  return *reinterpret_cast<const lds_v4f*>(stage + o.sa + 16 * mi * 4);
 }
 
 // Software pipeline over the MI x NJ MFMA tiles of a chunk, flattened as k = mi * NJ + nj:
@@ -266,7 +283,7 @@ struct ChunkState {
 };
 
 template <class C, int k>
-__device__ __forceinline__ void chunk_step(const uint8_t* stage, const FragOffsets<C>& o,
+__device__ __forceinline__ void chunk_step(const lds_u8* stage, const FragOffsets<C>& o,
                                            ChunkState<C>& st, float sb_blk,
                                            v4f (&acc)[C::MI][C::NJ]) {
   constexpr int kTiles = C::MI * C::NJ;
@@ -302,19 +319,19 @@ __device__ __forceinline__ void chunk_step(const uint8_t* stage, const FragOffse
 }
 
 template <class C, int nj>
-__device__ __forceinline__ void load_bf(const uint8_t* stage, const FragOffsets<C>& o,
+__device__ __forceinline__ void load_bf(const lds_u8* stage, const FragOffsets<C>& o,
                                         ChunkState<C>& st, float sb_blk) {
   if constexpr (nj < C::NJ) {
     st.bf[nj] = frag_b<C, nj>(stage, o);
     st.sbv[nj] =
-        C::kPerColScale ? *reinterpret_cast<const float*>(stage + o.sb + 64 * nj) : sb_blk;
+        C::kPerColScale ? *reinterpret_cast<const lds_f32*>(stage + o.sb + 64 * nj) : sb_blk;
     load_bf<C, nj + 1>(stage, o, st, sb_blk);
   }
 }
 
 // One 128-wide reduction chunk out of a landed stage.
 template <class C>
-__device__ __forceinline__ void compute_chunk(const uint8_t* stage, float sb_blk,
+__device__ __forceinline__ void compute_chunk(const lds_u8* stage, float sb_blk,
                                               const FragOffsets<C>& o,
                                               v4f (&acc)[C::MI][C::NJ]) {
   ChunkState<C> st;
@@ -330,7 +347,7 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A,
                                           const uint8_t* __restrict__ B,
                                           const float* __restrict__ sB, void* __restrict__ Cout,
                                           int64_t I, int64_t J, int64_t L, int accumulate,
-                                          uint8_t* stage0, uint8_t* stage1) {
+                                          lds_u8* stage0, lds_u8* stage1) {
   const int64_t tiles_i = (I + C::BM - 1) / C::BM;
   const int64_t tiles_j = (J + C::BN - 1) / C::BN;
   const int64_t nwg = tiles_i * tiles_j;
@@ -378,7 +395,7 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A,
   // last chunk is handled after the loop. Every half: wait for this wave's DMA, barrier (the
   // stage has landed for all waves, and the other stage is no longer being read), enqueue the
   // next chunk into the other stage, multiply out of this one.
-  auto half = [&](uint8_t* cur, uint8_t* nxt, int64_t c) {
+  auto half = [&](lds_u8* cur, lds_u8* nxt, int64_t c) {
     const float sb = sb_next;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -419,9 +436,16 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A,
   }
 }
 
+// Two tile shapes: 256x256 (8 waves of 128x64, one block per CU) for GEMMs with at least one
+// full wave of such tiles, and 128x128 (4 waves of 64x64, two blocks per CU) for GEMMs whose
+// output is too small to fill the chip with big tiles (e.g. the weight gradients of the
+// 2048-wide projections).
 using FwdBig = Cfg<kFwd, 256, 256, 2, 4>;
 using DgradBig = Cfg<kDgrad, 256, 256, 2, 4>;
 using WgradBig = Cfg<kWgrad, 256, 256, 2, 4>;
+using FwdSmall = Cfg<kFwd, 128, 128, 2, 2>;
+using DgradSmall = Cfg<kDgrad, 128, 128, 2, 2>;
+using WgradSmall = Cfg<kWgrad, 128, 128, 2, 2>;
 
 #define PURO_GEMM_KERNEL(NAME, CFG)                                                        \
   __global__ __launch_bounds__(CFG::kThreads) void NAME(                                   \
@@ -430,12 +454,23 @@ using WgradBig = Cfg<kWgrad, 256, 256, 2, 4>;
       int64_t I, int64_t J, int64_t L, int accumulate) {                                   \
     __shared__ __attribute__((aligned(1024))) uint8_t stage0[CFG::kStageBytes];            \
     __shared__ __attribute__((aligned(1024))) uint8_t stage1[CFG::kStageBytes];            \
-    gemm_body<CFG>(A, sA, B, sB, Cout, I, J, L, accumulate, stage0, stage1);               \
+    gemm_body<CFG>(A, sA, B, sB, Cout, I, J, L, accumulate, (lds_u8*)stage0,               \
+                   (lds_u8*)stage1);                                                        \
   }
 
 PURO_GEMM_KERNEL(gemm_fwd_256x256, FwdBig)
 PURO_GEMM_KERNEL(gemm_dgrad_256x256, DgradBig)
 PURO_GEMM_KERNEL(gemm_wgrad_256x256, WgradBig)
+PURO_GEMM_KERNEL(gemm_fwd_128x128, FwdSmall)
+PURO_GEMM_KERNEL(gemm_dgrad_128x128, DgradSmall)
+PURO_GEMM_KERNEL(gemm_wgrad_128x128, WgradSmall)
+
+// Number of compute units the big tiles must at least fill once.
+constexpr int64_t kComputeUnits = 256;
+
+inline bool use_big_tiles(int64_t I, int64_t J) {
+  return ((I + 255) / 256) * ((J + 255) / 256) >= kComputeUnits;
+}
 
 typedef void (*GemmKernel)(const uint8_t*, const float*, const uint8_t*, const float*, void*,
                            int64_t, int64_t, int64_t, int);
@@ -468,7 +503,9 @@ extern "C" puro_status puro_fp8_gemm_fwd(const void* xq, const float* sx, const 
   PURO_TRY(check_ptr(sw, red_empty));
   PURO_TRY(check_ptr(y, out_empty));
   if (out_empty) return PURO_OK;
-  return launch<FwdBig>(gemm_fwd_256x256, xq, sx, wq, sw, y, M, N, K, 0, stream);
+  if (use_big_tiles(M, N))
+    return launch<FwdBig>(gemm_fwd_256x256, xq, sx, wq, sw, y, M, N, K, 0, stream);
+  return launch<FwdSmall>(gemm_fwd_128x128, xq, sx, wq, sw, y, M, N, K, 0, stream);
 }
 
 extern "C" puro_status puro_fp8_gemm_dgrad(const void* dyq, const float* sdy, const void* wq,
@@ -483,7 +520,9 @@ extern "C" puro_status puro_fp8_gemm_dgrad(const void* dyq, const float* sdy, co
   PURO_TRY(check_ptr(sw, red_empty));
   PURO_TRY(check_ptr(dx, out_empty));
   if (out_empty) return PURO_OK;
-  return launch<DgradBig>(gemm_dgrad_256x256, dyq, sdy, wq, sw, dx, M, K, N, 0, stream);
+  if (use_big_tiles(M, K))
+    return launch<DgradBig>(gemm_dgrad_256x256, dyq, sdy, wq, sw, dx, M, K, N, 0, stream);
+  return launch<DgradSmall>(gemm_dgrad_128x128, dyq, sdy, wq, sw, dx, M, K, N, 0, stream);
 }
 
 extern "C" puro_status puro_fp8_gemm_wgrad(const void* dytq, const float* sdyt, const void* xtq,
@@ -499,6 +538,9 @@ extern "C" puro_status puro_fp8_gemm_wgrad(const void* dytq, const float* sdyt, 
   PURO_TRY(check_ptr(sxt, red_empty));
   PURO_TRY(check_ptr(dw, out_empty));
   if (out_empty) return PURO_OK;
-  return launch<WgradBig>(gemm_wgrad_256x256, dytq, sdyt, xtq, sxt, dw, N, K, M, accumulate,
-                          stream);
+  if (use_big_tiles(N, K))
+    return launch<WgradBig>(gemm_wgrad_256x256, dytq, sdyt, xtq, sxt, dw, N, K, M, accumulate,
+                            stream);
+  return launch<WgradSmall>(gemm_wgrad_128x128, dytq, sdyt, xtq, sxt, dw, N, K, M, accumulate,
+                            stream);
 }

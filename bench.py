@@ -40,8 +40,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--layers", type=int, default=28, help=argparse.SUPPRESS)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--no-kernel-events", action="store_true",
-                   help="time the step without per-kernel events")
+    p.add_argument("--no-graph", action="store_true",
+                   help="time eager launches instead of one captured HIP graph per step")
     return p.parse_args()
 
 
@@ -54,8 +54,10 @@ class Stack:
         from blockwise_fp8_gemm_x128_amd import synth
 
         dev = torch.device("cuda:0")
+        self.stream = torch.cuda.current_stream(dev)  # launches are bound to it when prepared
         self.launches = []  # (kernel class, flops, bytes, callable)
         shared = {}
+        self.shared = shared  # intermediates reused across layers: keep them allocated
 
         def buf(key, shape, dtype):
             if key not in shared:
@@ -106,6 +108,7 @@ class Stack:
                      B.prepare("puro_fp8_gemm_wgrad", dytq, sdyt, xtq, sxt, dw, M, N, K, 0)),
                 ])
         self.launches = fwd + [op for grp in reversed(bwd) for op in grp]
+        self.graph = None
         self.flops = sum(l[1] for l in self.launches)
         self.bytes = sum(l[2] for l in self.launches)
 
@@ -115,9 +118,19 @@ class Stack:
                 call()
         else:
             for (_, _, _, call), (e0, e1) in zip(self.launches, events):
-                e0.record()
+                e0.record(self.stream)
                 call()
-                e1.record()
+                e1.record(self.stream)
+
+    def capture(self):
+        """Capture one whole step (896 launches) as a HIP graph on the stack's stream."""
+        import torch
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph, stream=self.stream):
+            self.run()
+
+    def replay(self):
+        self.graph.replay()
 
 
 def cpu_baseline(M: int, layers: int, rows_fwd: int = 64, rows_wgrad: int = 8):
@@ -183,28 +196,47 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a HIP device"
     M = M_TOKENS
-    stack = Stack(args.layers, M)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):  # every launch is bound to this stream when prepared
+        stack = Stack(args.layers, M)
     torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        stack.run()
+    with torch.cuda.stream(side):
+        for _ in range(args.warmup):
+            stack.run()
     torch.cuda.synchronize()
+    use_graph = not args.no_graph
+    if use_graph:
+        stack.capture()
+        stack.replay()  # one untimed replay
+        torch.cuda.synchronize()
 
-    use_events = not args.no_kernel_events
-    ev_sets = []
-    if use_events:
-        for _ in range(args.steps):
-            ev_sets.append([(torch.cuda.Event(enable_timing=True),
-                             torch.cuda.Event(enable_timing=True)) for _ in stack.launches])
+    # Timed region: K whole steps (one graph replay each, or eager launches).
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
-        stack.run(ev_sets[k] if use_events else None)
+    with torch.cuda.stream(side):
+        for _ in range(args.steps):
+            if use_graph:
+                stack.replay()
+            else:
+                stack.run()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
 
+    # Kernel timing pass: the same K steps launched eagerly with a HIP event pair around every
+    # launch on the launch stream (events cannot be placed inside the replayed graph).
+    ev_sets = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in stack.launches] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    with torch.cuda.stream(side):
+        for k in range(args.steps):
+            stack.run(ev_sets[k])
+    torch.cuda.synchronize()
+    eager_ms_per_step = (time.perf_counter() - t1) * 1e3 / args.steps
+
     per_class = {}
-    if use_events:
+    if True:
         for evs in ev_sets:
             for (cls, fl, by, _), (e0, e1) in zip(stack.launches, evs):
                 d = per_class.setdefault(cls, {"ms": 0.0, "launches": 0, "flops": 0.0,
@@ -270,6 +302,8 @@ def main():
         "roofline_step_ms": roof_ms,
         "step_frac_of_roofline": roof_ms / ms_per_step,
         "kernel_event_sum_ms_per_step": gemm_ms + quant_ms,
+        "timed_region": "one captured HIP graph replay per step" if use_graph else "eager launches",
+        "kernel_timing_pass_ms_per_step": eager_ms_per_step,
         "kernels": kernels,
         "roofline": roofline,
     }

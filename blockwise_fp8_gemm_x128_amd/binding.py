@@ -144,9 +144,14 @@ def prepare(name: str, *args):
     stream = _stream(dev)
     conv.append(stream)
 
+    keep = tuple(a for a in args if isinstance(a, torch.Tensor))
+
     def call():
+        # `keep` holds the tensors: their device memory must outlive every launch of this call
+        # (including replays of a captured graph), not just the moment of preparation.
         st = fn(*conv)
         if st != 0:
             check(st)
 
+    call.tensors = keep
     return call

@@ -71,13 +71,14 @@ struct Cfg {
   static constexpr int kAOff = 0;
   static constexpr int kBOff = BM * kChunk;
   static constexpr int kSAOff = kBOff + BN * kChunk;
-  static constexpr int kSBOff = kSAOff + BM * 4;
-  static constexpr int kStageBytes = kSBOff + (kPerColScale ? BN * 4 : 0);
+  static constexpr int kScaleArea = 1024;  // one 64-lane x 16-byte DMA; rows beyond BM read 0
+  static constexpr int kSBOff = kSAOff + kScaleArea;
+  static constexpr int kStageBytes = kSBOff + (kPerColScale ? kScaleArea : 0);
   static_assert(BM % 128 == 0 && BN % 128 == 0, "tiles are whole 128x128 blocks");
   static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns lie in one 128-column block");
   static_assert(WM <= 128 && 128 % WM == 0, "a wave's rows lie in one 128-row half");
   static_assert((BM / 8) % kWaves == 0 && (BN / 8) % kWaves == 0, "even DMA split");
-  static_assert(BM / 4 <= 64 && BN / 4 <= 64, "one DMA instruction per scale row");
+  static_assert(BM * 4 <= kScaleArea && BN * 4 <= kScaleArea, "one DMA per scale row");
   static_assert(!kBTrans || WN == 64, "reduction-major B fragment offsets assume WN = 64");
 };
 
@@ -191,10 +192,13 @@ struct Loader {
               stage + C::kBOff + 8 * q * kChunk);
       }
     }
-    if (wave == 0 && lane < C::BM / 4)
-      dma16(make_rsrc(sA + c * I + i0, (I - i0) * 4), 16 * lane, 0, stage + C::kSAOff);
-    if (C::kPerColScale && wave == (1 % C::kWaves) && lane < C::BN / 4)
-      dma16(make_rsrc(sB + c * J + j0, (J - j0) * 4), 16 * lane, 0, stage + C::kSBOff);
+    // scale rows: all 64 lanes (no divergence); lanes past the tile's rows read zeros
+    if (wave == 0)
+      dma16(make_rsrc(sA + c * I + i0, imin64(I - i0, C::BM) * 4), 16 * lane, 0,
+            stage + C::kSAOff);
+    if (C::kPerColScale && wave == (1 % C::kWaves))
+      dma16(make_rsrc(sB + c * J + j0, imin64(J - j0, C::BN) * 4), 16 * lane, 0,
+            stage + C::kSBOff);
   }
 };
 

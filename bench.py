@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true",
                    help="time eager launches instead of one captured HIP graph per step")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     return p.parse_args()
 
 
@@ -92,19 +94,19 @@ class Stack:
                      B.prepare("puro_quant_w_128x128", w, N, K, wq, sw)),
                     ("quant_act_1x128", 0.0, M * K * B_ACT,
                      B.prepare("puro_quant_act_1x128", x, M, K, xq, sx)),
-                    ("gemm_fwd", f, 0.0,
+                    (f"gemm_fwd[{name}]", f, 0.0,
                      B.prepare("puro_fp8_gemm_fwd", xq, sx, wq, sw, y, M, N, K)),
                 ]
                 bwd.append([
                     ("quant_act_1x128", 0.0, M * N * B_ACT,
                      B.prepare("puro_quant_act_1x128", dy, M, N, dyq, sdy)),
-                    ("gemm_dgrad", f, 0.0,
+                    (f"gemm_dgrad[{name}]", f, 0.0,
                      B.prepare("puro_fp8_gemm_dgrad", dyq, sdy, wq, sw, dx, M, N, K)),
                     ("quant_transpose", 0.0, M * N * B_ACT,
                      B.prepare("puro_quant_transpose", dy, M, N, dytq, sdyt)),
                     ("quant_transpose", 0.0, M * K * B_ACT,
                      B.prepare("puro_quant_transpose", x, M, K, xtq, sxt)),
-                    ("gemm_wgrad", f, 0.0,
+                    (f"gemm_wgrad[{name}]", f, 0.0,
                      B.prepare("puro_fp8_gemm_wgrad", dytq, sdyt, xtq, sxt, dw, M, N, K, 0)),
                 ])
         self.launches = fwd + [op for grp in reversed(bwd) for op in grp]
@@ -170,10 +172,18 @@ def cpu_baseline(M: int, layers: int, rows_fwd: int = 64, rows_wgrad: int = 8):
         t3 = time.perf_counter()
         t_gemm += (t1 - t0) * M / rows_fwd + (t2 - t1) * M / rows_fwd + (t3 - t2) * N / rows_wgrad
     step_s = layers * (t_quant + t_gemm)
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")),
+                             None)
+    except OSError:
+        pass
     return {
         "value": M / step_s,
         "unit": "tokens/s",
         "cores": oracle.num_threads(),
+        "cpu_model": cpu_model,
         "kind": "oracle",
         "sample": (f"layer 0 of the step: all 5 quantiser passes per linear at full size "
                    f"(timed), each GEMM on {rows_fwd} sampled output rows (fwd, dgrad) or "
@@ -185,8 +195,54 @@ def cpu_baseline(M: int, layers: int, rows_fwd: int = 64, rows_wgrad: int = 8):
     }
 
 
+def copy_calibration():
+    """A plain streaming kernel of known size -- torch's elementwise negation over 2^28 fp32
+    (reads 1 GiB, writes 1 GiB) -- the reference against which the FETCH_SIZE / WRITE_SIZE
+    counters are scaled."""
+    import torch
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n}))
+
+
+def gemm_source_digest() -> str:
+    """Digest of the GEMM kernel sources, to tell whether stored counters still apply."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.hpp"):
+        with open(os.path.join(ROOT, "blockwise_fp8_gemm_x128_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_qwen3_1p7b_linear_stack_M8192.txt")
+
+
+def stored_traffic(kernel_class: str):
+    """HBM bytes per launch of `kernel_class` from the committed FETCH_SIZE / WRITE_SIZE summary
+    (its `traffic-record:` line, counters already scaled by the copy-kernel factors), or None if
+    there is none or the GEMM sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_SUMMARY) as fh:
+            recs = [json.loads(l.split(":", 1)[1]) for l in fh if l.startswith("traffic-record:")]
+    except (OSError, ValueError):
+        return None
+    for t in recs:
+        if t.get("source_digest") == gemm_source_digest() and t.get("kernel_class") == kernel_class:
+            return 1024.0 * (t["fetch_kib_per_launch"] * t["fetch_factor"] +
+                             t["write_kib_per_launch"] * t["write_factor"])
+    return None
+
+
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
               "(multi-GPU runs are out of scope: the path shards by data parallelism, see the "
@@ -263,13 +319,34 @@ def main():
         k = kernels[dom]
         if "tflops" in k:
             roofline = {"bound": "mfma", "achieved": k["tflops"], "peak": PEAK_FP8_TFLOPS,
-                        "unit": "TFLOP/s", "frac": k["frac_fp8_peak"], "traffic": None,
-                        "kernel": dom}
+                        "unit": "TFLOP/s", "frac": k["frac_fp8_peak"],
+                        "traffic": stored_traffic(dom),
+                        "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                        "scaled by a plain copy kernel)",
+                        "kernel": dom,
+                        "avg_launch_us": k["avg_launch_us"],
+                        "gemm_source_digest": gemm_source_digest()}
         else:
             roofline = {"bound": "hbm", "achieved": k["gbps"], "peak": PEAK_HBM_GBPS,
                         "unit": "GB/s", "frac": k["frac_hbm_peak"], "traffic": None,
                         "kernel": dom}
     gemm_ms = sum(v["ms_per_step"] for c, v in kernels.items() if c.startswith("gemm"))
+    by_kind = {}
+    for c, v in kernels.items():
+        kind = c.split("[")[0]
+        e = by_kind.setdefault(kind, {"ms_per_step": 0.0, "flops": 0.0, "bytes": 0.0})
+        e["ms_per_step"] += v["ms_per_step"]
+    for kind, e in by_kind.items():
+        fl = sum(l[1] for l in stack.launches if l[0].split("[")[0] == kind)
+        by = sum(l[2] for l in stack.launches if l[0].split("[")[0] == kind)
+        secs = e["ms_per_step"] * 1e-3
+        if fl:
+            e["tflops"] = fl / secs / 1e12
+            e["frac_fp8_peak"] = e["tflops"] / PEAK_FP8_TFLOPS
+        else:
+            e["gbps"] = by / secs / 1e9
+            e["frac_hbm_peak"] = e["gbps"] / PEAK_HBM_GBPS
+        del e["flops"], e["bytes"]
     quant_ms = sum(v["ms_per_step"] for c, v in kernels.items() if c.startswith("quant"))
     gemm_flops = sum(l[1] for l in stack.launches)
     quant_bytes = sum(l[2] for l in stack.launches)
@@ -304,6 +381,7 @@ def main():
         "kernel_event_sum_ms_per_step": gemm_ms + quant_ms,
         "timed_region": "one captured HIP graph replay per step" if use_graph else "eager launches",
         "kernel_timing_pass_ms_per_step": eager_ms_per_step,
+        "kernels_by_kind": by_kind,
         "kernels": kernels,
         "roofline": roofline,
     }

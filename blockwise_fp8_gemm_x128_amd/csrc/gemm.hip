@@ -31,6 +31,8 @@
 // remapped so that consecutive tiles run on one XCD (sharing that XCD's L2), and tiles are
 // walked in bands of 8 tile-rows, column by column, so concurrently running tiles share A and B
 // panels.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace puro {
@@ -74,8 +76,12 @@ struct Cfg {
   static constexpr int kScaleArea = 1024;  // one 64-lane x 16-byte DMA; rows beyond BM read 0
   static constexpr int kSBOff = kSAOff + kScaleArea;
   static constexpr int kStageBytes = kSBOff + (kPerColScale ? kScaleArea : 0);
-  static_assert(BM % 128 == 0 && BN % 128 == 0, "tiles are whole 128x128 blocks");
-  static_assert(WN <= 128 && 128 % WN == 0, "a wave's columns lie in one 128-column block");
+  // blocks that fit on one CU at once (160 KB of LDS, two stages per block)
+  static constexpr int kResident = (160 * 1024) / (2 * kStageBytes);
+  static_assert(BM % 128 == 0 && (BN % 128 == 0 || kPerColScale),
+                "block-scaled tiles are whole 128x128 blocks");
+  static_assert(WN % 16 == 0 && (kPerColScale || (WN <= 128 && 128 % WN == 0)),
+                "a wave's columns lie in one 128-column scale block");
   static_assert(WM <= 128 && 128 % WM == 0, "a wave's rows lie in one 128-row half");
   static_assert((BM / 8) % kWaves == 0 && (BN / 8) % kWaves == 0, "even DMA split");
   static_assert(BM * 4 <= kScaleArea && BN * 4 <= kScaleArea, "one DMA per scale row");
@@ -211,8 +217,8 @@ struct FragOffsets {
   int a[2];    // [half]: A rows, wave-relative
   int b[2];    // same for row-major B
   int bt[4];   // reduction-major B, per nj
-  int sa;      // this lane's 4 A scales (wave-relative)
-  int sb;      // this lane's B scale column base (per-column mode)
+  int sa;      // this lane's A scale (row r of each 16-row block)
+  int sb;      // this lane's 4 B scales (columns 4G..4G+3 of each 16-column block)
 
   __device__ __forceinline__ void init(int wm, int wn, int lane) {
     const int G = lane >> 4, r = lane & 15;
@@ -229,8 +235,8 @@ struct FragOffsets {
       const int piece = (((wn * C::WN) & 127) >> 4) + nj;
       bt[nj] = C::kBOff + slab + (32 * G + (r >> 1)) * kChunk + 8 * (r & 1) + ((piece ^ xs) << 4);
     }
-    sa = C::kSAOff + (wm * C::WM + 4 * G) * 4;
-    sb = C::kSBOff + (wn * C::WN + r) * 4;
+    sa = C::kSAOff + (wm * C::WM + r) * 4;
+    sb = C::kSBOff + (wn * C::WN + 4 * G) * 4;
   }
 };
 
@@ -267,23 +273,29 @@ __device__ __forceinline__ v8i frag_b(const lds_u8* stage, const FragOffsets<C>&
 }
 
 template <class C, int mi>
-__device__ __forceinline__ v4f scale_a(const lds_u8* stage, const FragOffsets<C>& o) {
-  return *reinterpret_cast<const lds_v4f*>(stage + o.sa + 16 * mi * 4);
+__device__ __forceinline__ float scale_a(const lds_u8* stage, const FragOffsets<C>& o) {
+  return *reinterpret_cast<const lds_f32*>(stage + o.sa + 16 * mi * 4);
 }
 
+// Each MFMA takes the B fragment as its row operand and the A fragment as its column operand,
+// so it produces the 16x16 block of C transposed: lane (G, r) receives C row r, columns
+// 4G..4G+3. A lane then needs one A scale per 16-row block and, in per-column mode, four B
+// scales per 16-column block, and its four results are adjacent in memory.
+//
 // Software pipeline over the MI x NJ MFMA tiles of a chunk, flattened as k = mi * NJ + nj:
 // step k issues MFMA k and then promotes MFMA k - NJ (same column, previous row block), whose
 // result is ready by then, so the promotion FMAs run on the vector ALU while the matrix core
 // works through the next products. Only NJ + 1 product vectors are live at once. The next row
-// block's A fragment and scales are fetched from LDS at the start of each row block.
+// block's A fragment and scale are fetched from LDS at the start of each row block.
 template <class C>
 struct ChunkState {
   static constexpr int kWin = C::NJ + 1;
+  using SB = typename std::conditional<C::kPerColScale, v4f, float>::type;
   v8i bf[C::NJ];
-  float sbv[C::NJ];
+  SB sbv[C::NJ];
   v4f p[kWin];
   v8i af_cur, af_next;
-  v4f sa_cur, sa_next, sa_prev;
+  float sa_cur, sa_next, sa_prev;
 };
 
 template <class C, int k>
@@ -299,13 +311,15 @@ __device__ __forceinline__ void chunk_step(const lds_u8* stage, const FragOffset
         st.af_next = frag_a<C, mi + 1>(stage, o);
         st.sa_next = scale_a<C, mi + 1>(stage, o);
       }
-      st.p[k % kWin] = mfma_fp8(st.af_cur, st.bf[nj]);
+      st.p[k % kWin] = mfma_fp8(st.bf[nj], st.af_cur);
     }
     if constexpr (k >= C::NJ) {
       constexpr int kp = k - C::NJ;
       constexpr int mp = kp / C::NJ, np = kp % C::NJ;
-      const v4f s = C::kPerColScale ? st.sa_prev * st.sbv[np] : st.sa_prev * sb_blk;
-      acc[mp][np] += s * st.p[kp % kWin];
+      if constexpr (C::kPerColScale)
+        acc[mp][np] += (st.sa_prev * st.sbv[np]) * st.p[kp % kWin];
+      else
+        acc[mp][np] += (st.sa_prev * sb_blk) * st.p[kp % kWin];
       // Pin the promoted accumulator here: without this, IR-level sinking defers whole chunks of
       // promotions past the next barrier and keeps their products live (register spills).
       asm volatile("" : "+v"(acc[mp][np]));
@@ -327,8 +341,10 @@ __device__ __forceinline__ void load_bf(const lds_u8* stage, const FragOffsets<C
                                         ChunkState<C>& st, float sb_blk) {
   if constexpr (nj < C::NJ) {
     st.bf[nj] = frag_b<C, nj>(stage, o);
-    st.sbv[nj] =
-        C::kPerColScale ? *reinterpret_cast<const lds_f32*>(stage + o.sb + 64 * nj) : sb_blk;
+    if constexpr (C::kPerColScale)
+      st.sbv[nj] = *reinterpret_cast<const lds_v4f*>(stage + o.sb + 64 * nj);
+    else
+      st.sbv[nj] = sb_blk;
     load_bf<C, nj + 1>(stage, o, st, sb_blk);
   }
 }
@@ -416,25 +432,26 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A,
   }
   if (c < nk) half(stage0, stage1, c);
 
-  // Epilogue: lane holds rows 4G+v and column c16 of every 16x16 tile.
-  const int G = lane >> 4, c16 = lane & 15;
+  // Epilogue: lane (G, r) holds row r, columns 4G..4G+3 of every 16x16 block: one 8-byte (bf16)
+  // or 16-byte (fp32) store per block.
+  const int G = lane >> 4, r16 = lane & 15;
   const int64_t r0 = i0 + wm * C::WM, q0 = j0 + wn * C::WN;
   if (r0 >= I || q0 >= J) return;  // this wave lies in the invalid half of an edge tile
 #pragma unroll
   for (int mi = 0; mi < C::MI; ++mi) {
 #pragma unroll
     for (int nj = 0; nj < C::NJ; ++nj) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t row = r0 + 16 * mi + 4 * G + v;
-        const int64_t col = q0 + 16 * nj + c16;
-        if (C::kOutF32) {
-          float* out = static_cast<float*>(Cout) + row * J + col;
-          *out = accumulate ? *out + acc[mi][nj][v] : acc[mi][nj][v];
-        } else {
-          uint16_t* out = static_cast<uint16_t*>(Cout) + row * J + col;
-          *out = static_cast<uint16_t>(f32_to_bf16_rne(acc[mi][nj][v]));
-        }
+      const int64_t row = r0 + 16 * mi + r16;
+      const int64_t col = q0 + 16 * nj + 4 * G;
+      const v4f v = acc[mi][nj];
+      if (C::kOutF32) {
+        v4f* out = reinterpret_cast<v4f*>(static_cast<float*>(Cout) + row * J + col);
+        *out = accumulate ? *out + v : v;
+      } else {
+        v2i packed;
+        packed[0] = static_cast<int>(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16));
+        packed[1] = static_cast<int>(f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16));
+        *reinterpret_cast<v2i*>(static_cast<uint16_t*>(Cout) + row * J + col) = packed;
       }
     }
   }
@@ -450,6 +467,9 @@ using WgradBig = Cfg<kWgrad, 256, 256, 2, 4>;
 using FwdSmall = Cfg<kFwd, 128, 128, 2, 2>;
 using DgradSmall = Cfg<kDgrad, 128, 128, 2, 2>;
 using WgradSmall = Cfg<kWgrad, 128, 128, 2, 2>;
+// Extra weight-gradient shape, 256x192 (8 waves of 128x48): a 2048 x 6144 output is then one
+// full round of 256 tiles instead of 1.5 rounds of 128x128 tiles.
+using WgradWide = Cfg<kWgrad, 256, 192, 2, 4>;
 
 #define PURO_GEMM_KERNEL(NAME, CFG)                                                        \
   __global__ __launch_bounds__(CFG::kThreads) void NAME(                                   \
@@ -468,12 +488,58 @@ PURO_GEMM_KERNEL(gemm_wgrad_256x256, WgradBig)
 PURO_GEMM_KERNEL(gemm_fwd_128x128, FwdSmall)
 PURO_GEMM_KERNEL(gemm_dgrad_128x128, DgradSmall)
 PURO_GEMM_KERNEL(gemm_wgrad_128x128, WgradSmall)
+PURO_GEMM_KERNEL(gemm_wgrad_256x192, WgradWide)
 
 // Number of compute units the big tiles must at least fill once.
 constexpr int64_t kComputeUnits = 256;
 
 inline bool use_big_tiles(int64_t I, int64_t J) {
   return ((I + 255) / 256) * ((J + 255) / 256) >= kComputeUnits;
+}
+
+// Compute units of the current device.
+inline int64_t device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    return kComputeUnits;
+  return cus;
+}
+
+// Weight-gradient tile shape: the candidate with the least estimated time, counting whole
+// rounds of tiles over the chip (a partial last round costs a full one), each tile's area,
+// the blocks resident per CU, and a per-shape efficiency measured on MI355X (bigger tiles
+// re-read less). 256x192 is only used when it tiles the output exactly.
+enum WgradShape { kW256x256, kW128x128, kW256x192 };
+
+inline WgradShape pick_wgrad_shape(int64_t I, int64_t J) {
+  struct Cand {
+    WgradShape shape;
+    int64_t bm, bn, resident;
+    double eff;
+    bool exact_only;
+  };
+  const Cand cands[] = {
+      {kW256x256, 256, 256, WgradBig::kResident, 1.00, false},
+      {kW128x128, 128, 128, WgradSmall::kResident, 0.85, false},
+      {kW256x192, 256, 192, WgradWide::kResident, 0.97, true},
+  };
+  const int64_t cus = device_cus();
+  WgradShape best = kW256x256;
+  double best_cost = -1.0;
+  for (const Cand& c : cands) {
+    if (c.exact_only && (I % c.bm != 0 || J % c.bn != 0)) continue;
+    const int64_t tiles = ((I + c.bm - 1) / c.bm) * ((J + c.bn - 1) / c.bn);
+    const int64_t slots = cus * c.resident;
+    const int64_t rounds = (tiles + slots - 1) / slots;
+    const double cost = static_cast<double>(rounds) * c.bm * c.bn * c.resident / c.eff;
+    if (best_cost < 0.0 || cost < best_cost) {
+      best_cost = cost;
+      best = c.shape;
+    }
+  }
+  return best;
 }
 
 typedef void (*GemmKernel)(const uint8_t*, const float*, const uint8_t*, const float*, void*,
@@ -542,9 +608,15 @@ extern "C" puro_status puro_fp8_gemm_wgrad(const void* dytq, const float* sdyt, 
   PURO_TRY(check_ptr(sxt, red_empty));
   PURO_TRY(check_ptr(dw, out_empty));
   if (out_empty) return PURO_OK;
-  if (use_big_tiles(N, K))
-    return launch<WgradBig>(gemm_wgrad_256x256, dytq, sdyt, xtq, sxt, dw, N, K, M, accumulate,
-                            stream);
-  return launch<WgradSmall>(gemm_wgrad_128x128, dytq, sdyt, xtq, sxt, dw, N, K, M, accumulate,
-                            stream);
+  switch (pick_wgrad_shape(N, K)) {
+    case kW256x256:
+      return launch<WgradBig>(gemm_wgrad_256x256, dytq, sdyt, xtq, sxt, dw, N, K, M,
+                              accumulate, stream);
+    case kW256x192:
+      return launch<WgradWide>(gemm_wgrad_256x192, dytq, sdyt, xtq, sxt, dw, N, K, M,
+                               accumulate, stream);
+    default:
+      return launch<WgradSmall>(gemm_wgrad_128x128, dytq, sdyt, xtq, sxt, dw, N, K, M,
+                                accumulate, stream);
+  }
 }

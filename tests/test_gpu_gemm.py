@@ -118,6 +118,23 @@ def test_wgrad_accumulate(puro, oracle):
     run_wgrad(puro, oracle, dy, x, dw0=dw0, what="wgrad accumulate")
 
 
+# Weight-gradient outputs chosen so that each tile shape the library picks from is used on a
+# 256-CU part: 128x128 (rows not a multiple of 256; and a 4096 x 2048 output), 256x192 (a
+# 2048 x 4608 output: one round instead of two); sampled output rows, overwrite and accumulate.
+WGRAD_SHAPES = [(256, 128, 384), (256, 4096, 2048), (256, 2048, 4608)]
+
+
+@pytest.mark.parametrize("M,N,K", WGRAD_SHAPES)
+@pytest.mark.parametrize("acc", [False, True])
+def test_wgrad_tile_shapes(puro, oracle, M, N, K, acc):
+    x = synth.randn_bf16((M, K), 1.0, 101 + N + K)
+    dy = synth.randn_bf16((M, N), 1e-3, 102 + N + K)
+    dw0 = (torch.randn((N, K), generator=torch.Generator().manual_seed(103)) * 1e-2
+           if acc else None)
+    run_wgrad(puro, oracle, dy, x, rows=sample_rows(N, 24, N + K), dw0=dw0,
+              what=f"wgrad tiles {M}x{N}x{K} acc={acc}")
+
+
 def test_zero_reduction(puro):
     say("zero reduction")
     xq = torch.empty((256, 0), dtype=torch.uint8, device="cuda")

@@ -2,9 +2,12 @@
 
 A step = 28 layers x 4 linear GEMM groups (qkv 2048->4096, o 2048->2048, gate_up 2048->12288,
 down 6144->2048) at M = 8192 tokens (2 sequences of 4096):
-  forward  (layer 0..27, qkv..down): quant_w_128x128(W), quant_act_1x128(X), fp8_gemm_fwd
-  backward (layer 27..0, down..qkv): quant_act_1x128(dY), fp8_gemm_dgrad,
-                                     quant_transpose(dY), quant_transpose(X), fp8_gemm_wgrad
+  forward  (layer 0..27, qkv..down): quant_w_128x128(W), quant_dual_1x128(X), fp8_gemm_fwd
+  backward (layer 27..0, down..qkv): quant_dual_1x128(dY), fp8_gemm_dgrad, fp8_gemm_wgrad
+quant_dual_1x128 writes both 1x128 orientations from one read: X's transposed copy is made in
+the forward pass and kept for the weight gradient. With --unfused the step instead runs
+quant_act_1x128(X) forward and quant_act_1x128(dY), quant_transpose(dY), quant_transpose(X)
+backward (same results, 2 more bytes read per element of X and dY).
 Every layer has its own seeded bf16 X, W, dY and fp32 dW buffers resident in HBM (~26 GB), so
 the 256 MB last-level cache cannot serve one layer's data to the next.
 
@@ -28,9 +31,11 @@ PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 M_TOKENS = 8192
 
-# algorithmic bytes per element of the quantisers: 2 B bf16 read + 1 B E4M3 write + scale share
+# algorithmic bytes per element of the quantisers: 2 B bf16 read + 1 B E4M3 write (per copy) +
+# scale share
 B_ACT = 2 + 1 + 4 / 128
 B_W = 2 + 1 + 4 / (128 * 128)
+B_DUAL = 2 + 2 * (1 + 4 / 128)
 
 
 def parse():
@@ -42,6 +47,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true",
                    help="time eager launches instead of one captured HIP graph per step")
+    p.add_argument("--unfused", action="store_true",
+                   help="separate quantiser launches per orientation instead of quant_dual_1x128")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     return p.parse_args()
@@ -50,7 +57,7 @@ def parse():
 class Stack:
     """Device buffers and pre-marshalled launches of the whole step."""
 
-    def __init__(self, layers: int, M: int):
+    def __init__(self, layers: int, M: int, fused: bool = True):
         import torch
         from blockwise_fp8_gemm_x128_amd import binding as B
         from blockwise_fp8_gemm_x128_amd import synth
@@ -85,30 +92,48 @@ class Stack:
                 dx = buf(("dx", M, K), (M, K), torch.bfloat16)
                 dytq = buf(("dytq", M, N), (N, M), torch.uint8)
                 sdyt = buf(("sdyt", M, N), (M // 128, N), torch.float32)
-                xtq = buf(("xtq", M, K), (K, M), torch.uint8)
-                sxt = buf(("sxt", M, K), (M // 128, K), torch.float32)
                 self.persist += [x, w, dy, wq, sw, dw]
                 f = 2.0 * M * N * K
-                fwd += [
-                    ("quant_w_128x128", 0.0, N * K * B_W,
-                     B.prepare("puro_quant_w_128x128", w, N, K, wq, sw)),
-                    ("quant_act_1x128", 0.0, M * K * B_ACT,
-                     B.prepare("puro_quant_act_1x128", x, M, K, xq, sx)),
-                    (f"gemm_fwd[{name}]", f, 0.0,
-                     B.prepare("puro_fp8_gemm_fwd", xq, sx, wq, sw, y, M, N, K)),
-                ]
-                bwd.append([
-                    ("quant_act_1x128", 0.0, M * N * B_ACT,
-                     B.prepare("puro_quant_act_1x128", dy, M, N, dyq, sdy)),
-                    (f"gemm_dgrad[{name}]", f, 0.0,
-                     B.prepare("puro_fp8_gemm_dgrad", dyq, sdy, wq, sw, dx, M, N, K)),
-                    ("quant_transpose", 0.0, M * N * B_ACT,
-                     B.prepare("puro_quant_transpose", dy, M, N, dytq, sdyt)),
-                    ("quant_transpose", 0.0, M * K * B_ACT,
-                     B.prepare("puro_quant_transpose", x, M, K, xtq, sxt)),
-                    (f"gemm_wgrad[{name}]", f, 0.0,
-                     B.prepare("puro_fp8_gemm_wgrad", dytq, sdyt, xtq, sxt, dw, M, N, K, 0)),
-                ])
+                q_w = ("quant_w_128x128", 0.0, N * K * B_W,
+                       B.prepare("puro_quant_w_128x128", w, N, K, wq, sw))
+                g_fwd = (f"gemm_fwd[{name}]", f, 0.0,
+                         B.prepare("puro_fp8_gemm_fwd", xq, sx, wq, sw, y, M, N, K))
+                g_dgrad = (f"gemm_dgrad[{name}]", f, 0.0,
+                           B.prepare("puro_fp8_gemm_dgrad", dyq, sdy, wq, sw, dx, M, N, K))
+                if fused:
+                    # X's transposed copy lives from this layer's forward to its backward
+                    xtq = torch.empty((K, M), dtype=torch.uint8, device=dev)
+                    sxt = torch.empty((M // 128, K), dtype=torch.float32, device=dev)
+                    self.persist += [xtq, sxt]
+                    fwd += [q_w,
+                            ("quant_dual_1x128", 0.0, M * K * B_DUAL,
+                             B.prepare("puro_quant_dual_1x128", x, M, K, xq, sx, xtq, sxt)),
+                            g_fwd]
+                    bwd.append([
+                        ("quant_dual_1x128", 0.0, M * N * B_DUAL,
+                         B.prepare("puro_quant_dual_1x128", dy, M, N, dyq, sdy, dytq, sdyt)),
+                        g_dgrad,
+                        (f"gemm_wgrad[{name}]", f, 0.0,
+                         B.prepare("puro_fp8_gemm_wgrad", dytq, sdyt, xtq, sxt, dw, M, N, K, 0)),
+                    ])
+                else:
+                    xtq = buf(("xtq", M, K), (K, M), torch.uint8)
+                    sxt = buf(("sxt", M, K), (M // 128, K), torch.float32)
+                    fwd += [q_w,
+                            ("quant_act_1x128", 0.0, M * K * B_ACT,
+                             B.prepare("puro_quant_act_1x128", x, M, K, xq, sx)),
+                            g_fwd]
+                    bwd.append([
+                        ("quant_act_1x128", 0.0, M * N * B_ACT,
+                         B.prepare("puro_quant_act_1x128", dy, M, N, dyq, sdy)),
+                        g_dgrad,
+                        ("quant_transpose", 0.0, M * N * B_ACT,
+                         B.prepare("puro_quant_transpose", dy, M, N, dytq, sdyt)),
+                        ("quant_transpose", 0.0, M * K * B_ACT,
+                         B.prepare("puro_quant_transpose", x, M, K, xtq, sxt)),
+                        (f"gemm_wgrad[{name}]", f, 0.0,
+                         B.prepare("puro_fp8_gemm_wgrad", dytq, sdyt, xtq, sxt, dw, M, N, K, 0)),
+                    ])
         self.launches = fwd + [op for grp in reversed(bwd) for op in grp]
         self.graph = None
         self.flops = sum(l[1] for l in self.launches)
@@ -125,7 +150,7 @@ class Stack:
                 e1.record(self.stream)
 
     def capture(self):
-        """Capture one whole step (896 launches) as a HIP graph on the stack's stream."""
+        """Capture one whole step (all its launches) as a HIP graph on the stack's stream."""
         import torch
         self.graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(self.graph, stream=self.stream):
@@ -254,7 +279,7 @@ def main():
     M = M_TOKENS
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):  # every launch is bound to this stream when prepared
-        stack = Stack(args.layers, M)
+        stack = Stack(args.layers, M, fused=not args.unfused)
     torch.cuda.synchronize()
     with torch.cuda.stream(side):
         for _ in range(args.warmup):
@@ -369,7 +394,9 @@ def main():
                                "{qkv 2048->4096, o 2048->2048, gate_up 2048->12288, "
                                "down 6144->2048}, fwd + dgrad + wgrad + all quantisers",
                    "tokens_per_step": M, "seqs": M // 4096, "seq_len": 4096,
-                   "layers": args.layers, "parallelism": "single GPU"},
+                   "layers": args.layers, "parallelism": "single GPU",
+                   "quantisers": ("separate per orientation" if args.unfused else
+                                  "fused two-orientation 1x128 for X and dY")},
         "gemm_tflops": gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None,
         "gemm_frac_fp8_peak": (gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS
                                if gemm_ms else None),

@@ -20,6 +20,7 @@ SIGNATURES = {
     "puro_quant_act_1x128": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "puro_quant_w_128x128": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "puro_quant_transpose": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
+    "puro_quant_dual_1x128": ([_P, _I64, _I64, _P, _P, _P, _P, _P], ctypes.c_int),
     "puro_fp8_gemm_fwd": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "puro_fp8_gemm_dgrad": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "puro_fp8_gemm_wgrad": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P],

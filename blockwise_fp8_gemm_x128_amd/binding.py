@@ -80,6 +80,22 @@ def puro_quant_transpose(x: torch.Tensor, qt=None, st=None):
     return qt, st
 
 
+def puro_quant_dual_1x128(x: torch.Tensor, q=None, s=None, qt=None, st=None):
+    """x bf16 [rows, cols] -> (q [rows, cols], s [cols/128, rows], qt [cols, rows],
+    st [rows/128, cols]): the outputs of puro_quant_act_1x128 and puro_quant_transpose from one
+    read of x."""
+    dev = _dev(x)
+    rows, cols = x.shape
+    _need(x, "x", torch.bfloat16, (rows, cols), dev)
+    q = _out(q, "q", FP8, (rows, cols), dev)
+    s = _out(s, "s", torch.float32, (cols // 128, rows), dev)
+    qt = _out(qt, "qt", FP8, (cols, rows), dev)
+    st = _out(st, "st", torch.float32, (rows // 128, cols), dev)
+    check(lib().puro_quant_dual_1x128(x.data_ptr(), rows, cols, q.data_ptr(), s.data_ptr(),
+                                      qt.data_ptr(), st.data_ptr(), _stream(dev)))
+    return q, s, qt, st
+
+
 def puro_fp8_gemm_fwd(xq, sx, wq, sw, y=None):
     """Y bf16 [M, N] from xq [M, K], sx [K/128, M], wq [N, K], sw [N/128, K/128]."""
     dev = _dev(xq)

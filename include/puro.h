@@ -84,6 +84,19 @@ puro_status puro_quant_w_128x128(const void* w, int64_t n, int64_t k, void* q, f
 puro_status puro_quant_transpose(const void* x, int64_t rows, int64_t cols, void* qt, float* st,
                                  void* stream);
 
+/* Both 1x128 orientations of one bf16 matrix from a single read of it: the row groups of
+ * puro_quant_act_1x128 and the column groups of puro_quant_transpose, bit for bit the same
+ * outputs as those two calls. The same passage defines both (groups of 128 along the reduction
+ * dimension of the GEMM that consumes each copy): an activation X feeds the forward GEMM
+ * (reduction over its columns) and the weight-gradient GEMM (reduction over its rows), and so
+ * does an output gradient dY for the data-gradient and weight-gradient GEMMs.
+ *   x   bf16 [rows][cols]       (input)
+ *   q   e4m3 [rows][cols], s  fp32 [cols/128][rows]   (as puro_quant_act_1x128)
+ *   qt  e4m3 [cols][rows], st fp32 [rows/128][cols]   (as puro_quant_transpose)
+ * The four outputs must not overlap each other or x. */
+puro_status puro_quant_dual_1x128(const void* x, int64_t rows, int64_t cols, void* q, float* s,
+                                  void* qt, float* st, void* stream);
+
 /* Forward GEMM  Y[m][n] = sum_kb sx[kb][m] * sw[n/128][kb] * sum_{k in kb} xq[m][k] * wq[n][k].
  *   xq e4m3 [M][K], sx fp32 [K/128][M]      (from puro_quant_act_1x128 of X)
  *   wq e4m3 [N][K], sw fp32 [N/128][K/128]  (from puro_quant_w_128x128 of W)

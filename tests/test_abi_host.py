@@ -69,6 +69,18 @@ def test_quant_validation(L, fn):
     assert f(None, 256, 0, None, None, None) == 0
 
 
+def test_dual_quant_validation(L):
+    f = L.puro_quant_dual_1x128
+    assert f(FAKE, 100, 128, FAKE, FAKE, FAKE, FAKE, None) == 2    # ragged rows
+    assert f(FAKE, 128, 200, FAKE, FAKE, FAKE, FAKE, None) == 2    # ragged cols
+    assert f(FAKE, 1 << 25, 128, FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert f(None, 128, 128, FAKE, FAKE, FAKE, FAKE, None) == 1    # NULL input
+    assert f(FAKE, 128, 128, FAKE, FAKE, None, FAKE, None) == 1    # NULL transposed payload
+    assert f(FAKE, 128, 128, FAKE, FAKE, FAKE, None, None) == 1    # NULL transposed scales
+    assert f(FAKE, 128, 128, FAKE, FAKE, FAKE, MIS, None) == 3     # misaligned
+    assert f(None, 0, 128, None, None, None, None, None) == 0      # empty: nothing to do
+
+
 def test_gemm_validation(L):
     fwd, dgrad, wgrad = L.puro_fp8_gemm_fwd, L.puro_fp8_gemm_dgrad, L.puro_fp8_gemm_wgrad
     for f in (fwd, dgrad):

@@ -1,4 +1,4 @@
-"""GPU parity of the three quantisers: payload bytes and scales must equal the oracle's bit for
+"""GPU parity of the quantisers (including the fused two-orientation one): payload bytes and scales must equal the oracle's bit for
 bit, on the tiny configuration, multi-tile and ragged shapes, special values, every bf16 value
 of the representable range, and the full-size Qwen3-1.7B layer shapes (M = 4096 and 16384) and
 the outlier stress inputs."""
@@ -53,12 +53,17 @@ def check_all_three(puro, oracle, x, what, weight=True, transpose=True):
     assert_same(gq, gs, oq, os_, what + " act")
     if weight:
         gq, gs = gpu_w(puro, x)
-        oq, os_ = oracle.quant_w_128x128(xn)
-        assert_same(gq, gs, oq, os_, what + " w")
+        wq, ws = oracle.quant_w_128x128(xn)
+        assert_same(gq, gs, wq, ws, what + " w")
     if transpose:
         gq, gs = gpu_tr(puro, x)
-        oq, os_ = oracle.quant_transpose(xn)
-        assert_same(gq, gs, oq, os_, what + " transpose")
+        tq, ts = oracle.quant_transpose(xn)
+        assert_same(gq, gs, tq, ts, what + " transpose")
+        # the fused quantiser: both orientations from one read, same bytes as the oracle's two
+        dq, ds, dqt, dst = puro.puro_quant_dual_1x128(x.cuda())
+        torch.cuda.synchronize()
+        assert_same(dq.cpu().numpy(), ds.cpu().numpy(), oq, os_, what + " dual rows")
+        assert_same(dqt.cpu().numpy(), dst.cpu().numpy(), tq, ts, what + " dual columns")
 
 
 def test_tiny_config(puro, oracle):
@@ -138,3 +143,5 @@ def test_empty(puro):
     x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
     q, s = puro.puro_quant_act_1x128(x)
     assert q.shape == (0, 256) and s.shape == (2, 0)
+    q, s, qt, st = puro.puro_quant_dual_1x128(x)
+    assert q.shape == (0, 256) and s.shape == (2, 0) and qt.shape == (256, 0) and st.shape == (0, 256)

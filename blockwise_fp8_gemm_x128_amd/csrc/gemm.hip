@@ -76,8 +76,6 @@ struct Cfg {
   static constexpr int kScaleArea = 1024;  // one 64-lane x 16-byte DMA; rows beyond BM read 0
   static constexpr int kSBOff = kSAOff + kScaleArea;
   static constexpr int kStageBytes = kSBOff + (kPerColScale ? kScaleArea : 0);
-  // blocks that fit on one CU at once (160 KB of LDS, two stages per block)
-  static constexpr int kResident = (160 * 1024) / (2 * kStageBytes);
   static_assert(BM % 128 == 0 && (BN % 128 == 0 || kPerColScale),
                 "block-scaled tiles are whole 128x128 blocks");
   static_assert(WN % 16 == 0 && (kPerColScale || (WN <= 128 && 128 % WN == 0)),
@@ -509,8 +507,9 @@ inline int64_t device_cus() {
 
 // Weight-gradient tile shape: the candidate with the least estimated time, counting whole
 // rounds of tiles over the chip (a partial last round costs a full one), each tile's area,
-// the blocks resident per CU, and a per-shape efficiency measured on MI355X (bigger tiles
-// re-read less). 256x192 is only used when it tiles the output exactly.
+// the blocks resident per CU (LDS and registers allow one 8-wave block of the 256-row shapes
+// or two 4-wave 128x128 blocks), and a per-shape efficiency measured on MI355X (bigger tiles
+// re-read less). The 256-row shapes are only used when they tile the output exactly.
 enum WgradShape { kW256x256, kW128x128, kW256x192 };
 
 inline WgradShape pick_wgrad_shape(int64_t I, int64_t J) {
@@ -521,9 +520,9 @@ inline WgradShape pick_wgrad_shape(int64_t I, int64_t J) {
     bool exact_only;
   };
   const Cand cands[] = {
-      {kW256x256, 256, 256, WgradBig::kResident, 1.00, false},
-      {kW128x128, 128, 128, WgradSmall::kResident, 0.85, false},
-      {kW256x192, 256, 192, WgradWide::kResident, 0.97, true},
+      {kW256x256, 256, 256, 1, 1.00, true},
+      {kW128x128, 128, 128, 2, 0.85, false},
+      {kW256x192, 256, 192, 1, 0.97, true},
   };
   const int64_t cus = device_cus();
   WgradShape best = kW256x256;

@@ -135,6 +135,19 @@ def test_wgrad_tile_shapes(puro, oracle, M, N, K, acc):
               what=f"wgrad tiles {M}x{N}x{K} acc={acc}")
 
 
+def test_big_tiles_with_ragged_edge(puro, oracle):
+    # 16512 = 64.5 x 256 rows: enough 256x256 tiles for the big-tile kernels, whose last tile
+    # row is half outside the output; the sampled rows include that half tile.
+    M, N, K = 16512, 1024, 256
+    x = synth.randn_bf16((M, K), 1.0, 111)
+    w = synth.randn_bf16((N, K), 0.02, 112)
+    dy = synth.randn_bf16((M, N), 1e-3, 113)
+    rows = np.unique(np.concatenate([sample_rows(M, 16, 114), np.arange(M - 130, M)]))
+    run_fwd(puro, oracle, x, w, rows=rows, what="fwd ragged big tiles")
+    w2 = synth.randn_bf16((N, 1024), 0.02, 115)
+    run_dgrad(puro, oracle, dy, w2, rows=rows, what="dgrad ragged big tiles")
+
+
 def test_zero_reduction(puro):
     say("zero reduction")
     xq = torch.empty((256, 0), dtype=torch.uint8, device="cuda")

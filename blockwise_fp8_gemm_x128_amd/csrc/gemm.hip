@@ -76,11 +76,11 @@ struct Cfg {
   static constexpr int kScaleArea = 1024;  // one 64-lane x 16-byte DMA; rows beyond BM read 0
   static constexpr int kSBOff = kSAOff + kScaleArea;
   static constexpr int kStageBytes = kSBOff + (kPerColScale ? kScaleArea : 0);
-  static_assert(BM % 128 == 0 && (BN % 128 == 0 || kPerColScale),
+  static_assert((BM % 128 == 0 && BN % 128 == 0) || kPerColScale,
                 "block-scaled tiles are whole 128x128 blocks");
   static_assert(WN % 16 == 0 && (kPerColScale || (WN <= 128 && 128 % WN == 0)),
                 "a wave's columns lie in one 128-column scale block");
-  static_assert(WM <= 128 && 128 % WM == 0, "a wave's rows lie in one 128-row half");
+  static_assert(WM <= 128 && WM % 16 == 0, "a wave's rows are whole 16-row fragments");
   static_assert((BM / 8) % kWaves == 0 && (BN / 8) % kWaves == 0, "even DMA split");
   static_assert(BM * 4 <= kScaleArea && BN * 4 <= kScaleArea, "one DMA per scale row");
   static_assert(!kBTrans || WN == 64, "reduction-major B fragment offsets assume WN = 64");
@@ -465,9 +465,11 @@ using WgradBig = Cfg<kWgrad, 256, 256, 2, 4>;
 using FwdSmall = Cfg<kFwd, 128, 128, 2, 2>;
 using DgradSmall = Cfg<kDgrad, 128, 128, 2, 2>;
 using WgradSmall = Cfg<kWgrad, 128, 128, 2, 2>;
-// Extra weight-gradient shape, 256x192 (8 waves of 128x48): a 2048 x 6144 output is then one
-// full round of 256 tiles instead of 1.5 rounds of 128x128 tiles.
+// Extra weight-gradient shapes that make common outputs whole rounds of tiles: 256x192 (8 waves
+// of 128x48; a 2048 x 6144 output is 256 tiles) and 192x256 (8 waves of 96x64; a 12288 x 2048
+// output is 512 tiles).
 using WgradWide = Cfg<kWgrad, 256, 192, 2, 4>;
+using WgradTall = Cfg<kWgrad, 192, 256, 2, 4>;
 
 #define PURO_GEMM_KERNEL(NAME, CFG)                                                        \
   __global__ __launch_bounds__(CFG::kThreads) void NAME(                                   \
@@ -487,6 +489,7 @@ PURO_GEMM_KERNEL(gemm_fwd_128x128, FwdSmall)
 PURO_GEMM_KERNEL(gemm_dgrad_128x128, DgradSmall)
 PURO_GEMM_KERNEL(gemm_wgrad_128x128, WgradSmall)
 PURO_GEMM_KERNEL(gemm_wgrad_256x192, WgradWide)
+PURO_GEMM_KERNEL(gemm_wgrad_192x256, WgradTall)
 
 // Number of compute units the big tiles must at least fill once.
 constexpr int64_t kComputeUnits = 256;
@@ -509,8 +512,8 @@ inline int64_t device_cus() {
 // rounds of tiles over the chip (a partial last round costs a full one), each tile's area,
 // the blocks resident per CU (LDS and registers allow one 8-wave block of the 256-row shapes
 // or two 4-wave 128x128 blocks), and a per-shape efficiency measured on MI355X (bigger tiles
-// re-read less). The 256-row shapes are only used when they tile the output exactly.
-enum WgradShape { kW256x256, kW128x128, kW256x192 };
+// re-read less). The 192- and 256-wide shapes are only used when they tile the output exactly.
+enum WgradShape { kW256x256, kW128x128, kW256x192, kW192x256 };
 
 inline WgradShape pick_wgrad_shape(int64_t I, int64_t J) {
   struct Cand {
@@ -523,6 +526,7 @@ inline WgradShape pick_wgrad_shape(int64_t I, int64_t J) {
       {kW256x256, 256, 256, 1, 1.00, true},
       {kW128x128, 128, 128, 2, 0.85, false},
       {kW256x192, 256, 192, 1, 0.97, true},
+      {kW192x256, 192, 256, 1, 0.97, true},
   };
   const int64_t cus = device_cus();
   WgradShape best = kW256x256;
@@ -613,6 +617,9 @@ extern "C" puro_status puro_fp8_gemm_wgrad(const void* dytq, const float* sdyt, 
                               accumulate, stream);
     case kW256x192:
       return launch<WgradWide>(gemm_wgrad_256x192, dytq, sdyt, xtq, sxt, dw, N, K, M,
+                               accumulate, stream);
+    case kW192x256:
+      return launch<WgradTall>(gemm_wgrad_192x256, dytq, sdyt, xtq, sxt, dw, N, K, M,
                                accumulate, stream);
     default:
       return launch<WgradSmall>(gemm_wgrad_128x128, dytq, sdyt, xtq, sxt, dw, N, K, M,

@@ -120,8 +120,9 @@ def test_wgrad_accumulate(puro, oracle):
 
 # Weight-gradient outputs chosen so that each tile shape the library picks from is used on a
 # 256-CU part: 128x128 (rows not a multiple of 256; and a 4096 x 2048 output), 256x192 (a
-# 2048 x 4608 output: one round instead of two); sampled output rows, overwrite and accumulate.
-WGRAD_SHAPES = [(256, 128, 384), (256, 4096, 2048), (256, 2048, 4608)]
+# 2048 x 4608 output: one round instead of two), 192x256 (a 12288 x 2048 output: two rounds of
+# 512 tiles); sampled output rows, overwrite and accumulate.
+WGRAD_SHAPES = [(256, 128, 384), (256, 4096, 2048), (256, 2048, 4608), (256, 12288, 2048)]
 
 
 @pytest.mark.parametrize("M,N,K", WGRAD_SHAPES)

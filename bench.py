@@ -2,7 +2,8 @@
 
 A step = 28 layers x 4 linear GEMM groups (qkv 2048->4096, o 2048->2048, gate_up 2048->12288,
 down 6144->2048) at M = 8192 tokens (2 sequences of 4096):
-  forward  (layer 0..27, qkv..down): quant_w_128x128(W), quant_dual_1x128(X), fp8_gemm_fwd
+  forward  (layer 0..27): quant_w_128x128_group(the layer's four W), then per linear
+                         (qkv..down): quant_dual_1x128(X), fp8_gemm_fwd
   backward (layer 27..0, down..qkv): quant_dual_1x128(dY), fp8_gemm_dgrad, fp8_gemm_wgrad
 quant_dual_1x128 writes both 1x128 orientations from one read: X's transposed copy is made in
 the forward pass and kept for the weight gradient. With --unfused the step instead runs
@@ -76,6 +77,9 @@ class Stack:
         self.persist = []
         fwd, bwd = [], []
         for layer in range(layers):
+            group_w, group_q, group_s = [], [], []
+            fwd.append(None)  # the layer's grouped weight quantisation, filled in below
+            wslot = len(fwd) - 1
             for li, (name, K, N) in enumerate(synth.LINEARS):
                 s = lambda kind: synth.stack_seed(layer, li, kind)  # noqa: E731
                 x = synth.randn_bf16((M, K), synth.X_STD, s(synth.KIND_X), dev)
@@ -94,8 +98,9 @@ class Stack:
                 sdyt = buf(("sdyt", M, N), (M // 128, N), torch.float32)
                 self.persist += [x, w, dy, wq, sw, dw]
                 f = 2.0 * M * N * K
-                q_w = ("quant_w_128x128", 0.0, N * K * B_W,
-                       B.prepare("puro_quant_w_128x128", w, N, K, wq, sw))
+                group_w.append(w)
+                group_q.append(wq)
+                group_s.append(sw)
                 g_fwd = (f"gemm_fwd[{name}]", f, 0.0,
                          B.prepare("puro_fp8_gemm_fwd", xq, sx, wq, sw, y, M, N, K))
                 g_dgrad = (f"gemm_dgrad[{name}]", f, 0.0,
@@ -105,8 +110,7 @@ class Stack:
                     xtq = torch.empty((K, M), dtype=torch.uint8, device=dev)
                     sxt = torch.empty((M // 128, K), dtype=torch.float32, device=dev)
                     self.persist += [xtq, sxt]
-                    fwd += [q_w,
-                            ("quant_dual_1x128", 0.0, M * K * B_DUAL,
+                    fwd += [("quant_dual_1x128", 0.0, M * K * B_DUAL,
                              B.prepare("puro_quant_dual_1x128", x, M, K, xq, sx, xtq, sxt)),
                             g_fwd]
                     bwd.append([
@@ -119,8 +123,7 @@ class Stack:
                 else:
                     xtq = buf(("xtq", M, K), (K, M), torch.uint8)
                     sxt = buf(("sxt", M, K), (M // 128, K), torch.float32)
-                    fwd += [q_w,
-                            ("quant_act_1x128", 0.0, M * K * B_ACT,
+                    fwd += [("quant_act_1x128", 0.0, M * K * B_ACT,
                              B.prepare("puro_quant_act_1x128", x, M, K, xq, sx)),
                             g_fwd]
                     bwd.append([
@@ -134,6 +137,11 @@ class Stack:
                         (f"gemm_wgrad[{name}]", f, 0.0,
                          B.prepare("puro_fp8_gemm_wgrad", dytq, sdyt, xtq, sxt, dw, M, N, K, 0)),
                     ])
+            # all four weights of the layer in one grouped launch
+            items = B.w_group_items(group_w, group_q, group_s)
+            fwd[wslot] = ("quant_w_128x128", 0.0,
+                          sum(w.shape[0] * w.shape[1] for w in group_w) * B_W,
+                          B.prepare("puro_quant_w_128x128_group", items, len(group_w)))
         self.launches = fwd + [op for grp in reversed(bwd) for op in grp]
         self.graph = None
         self.flops = sum(l[1] for l in self.launches)

@@ -14,6 +14,14 @@ _lib = None
 # Every symbol declared in include/puro.h, with its ctypes signature.
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
+W_GROUP_MAX = 8  # PURO_W_GROUP_MAX
+
+
+class PuroWItem(ctypes.Structure):
+    """puro_w_item: one weight matrix of a grouped 128x128 quantisation."""
+    _fields_ = [("w", ctypes.c_void_p), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
+                ("q", ctypes.c_void_p), ("s", ctypes.c_void_p)]
+
 SIGNATURES = {
     "puro_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "puro_abi_version": ([], ctypes.c_int),
@@ -21,6 +29,7 @@ SIGNATURES = {
     "puro_quant_w_128x128": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "puro_quant_transpose": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "puro_quant_dual_1x128": ([_P, _I64, _I64, _P, _P, _P, _P, _P], ctypes.c_int),
+    "puro_quant_w_128x128_group": ([ctypes.POINTER(PuroWItem), ctypes.c_int, _P], ctypes.c_int),
     "puro_fp8_gemm_fwd": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "puro_fp8_gemm_dgrad": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "puro_fp8_gemm_wgrad": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P],

@@ -9,7 +9,7 @@ from __future__ import annotations
 
 import torch
 
-from ._lib import PuroError, check, lib
+from ._lib import W_GROUP_MAX, PuroError, PuroWItem, check, lib
 
 FP8 = torch.uint8  # E4M3 codes travel as raw bytes
 
@@ -66,6 +66,37 @@ def puro_quant_w_128x128(w: torch.Tensor, q=None, s=None):
     check(lib().puro_quant_w_128x128(w.data_ptr(), n, k, q.data_ptr(), s.data_ptr(),
                                      _stream(dev)))
     return q, s
+
+
+def w_group_items(ws, qs, ss):
+    """ctypes array of puro_w_item for weights ws [n, k] and outputs qs, ss (checked)."""
+    if len(ws) > W_GROUP_MAX:
+        raise PuroError(f"at most {W_GROUP_MAX} matrices per grouped call")
+    if not (len(ws) == len(qs) == len(ss)):
+        raise PuroError("ws, qs and ss must have the same length")
+    items = (PuroWItem * max(len(ws), 1))()
+    for i, (w, q, s) in enumerate(zip(ws, qs, ss)):
+        dev = _dev(w)
+        n, k = w.shape
+        _need(w, f"w[{i}]", torch.bfloat16, (n, k), dev)
+        _need(q, f"q[{i}]", FP8, (n, k), dev)
+        _need(s, f"s[{i}]", torch.float32, (n // 128, k // 128), dev)
+        items[i] = PuroWItem(w.data_ptr(), n, k, q.data_ptr(), s.data_ptr())
+    return items
+
+
+def puro_quant_w_128x128_group(ws, qs=None, ss=None):
+    """Several bf16 weights [n, k] quantised in one launch -> (list of q, list of s), each as
+    from puro_quant_w_128x128."""
+    if not ws:
+        return [], []
+    dev = _dev(ws[0])
+    qs = qs or [torch.empty(w.shape, dtype=FP8, device=dev) for w in ws]
+    ss = ss or [torch.empty((w.shape[0] // 128, w.shape[1] // 128), dtype=torch.float32,
+                            device=dev) for w in ws]
+    items = w_group_items(ws, qs, ss)
+    check(lib().puro_quant_w_128x128_group(items, len(ws), _stream(dev)))
+    return qs, ss
 
 
 def puro_quant_transpose(x: torch.Tensor, qt=None, st=None):
@@ -160,7 +191,7 @@ def prepare(name: str, *args):
     stream = _stream(dev)
     conv.append(stream)
 
-    keep = tuple(a for a in args if isinstance(a, torch.Tensor))
+    keep = tuple(args)  # tensors and ctypes arrays the raw arguments point into
 
     def call():
         # `keep` holds the tensors: their device memory must outlive every launch of this call

@@ -61,14 +61,12 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t* __
 
 // ------------------------------------------------------------------ 128x128 weight blocks
 // One 256-thread block per 128x128 block: 16 lanes cover a 256 B row, 8 passes of 16 rows.
-__global__ __launch_bounds__(256) void quant_w_128x128_kernel(const uint16_t* __restrict__ w,
-                                                              int64_t n, int64_t k,
-                                                              uint8_t* __restrict__ q,
-                                                              float* __restrict__ s) {
-  __shared__ float wave_max[4];
+__device__ __forceinline__ void quant_w_block(const uint16_t* __restrict__ w, int64_t n, int64_t k,
+                                              uint8_t* __restrict__ q, float* __restrict__ s,
+                                              int64_t blk, float* wave_max) {
   const int64_t kblocks = k >> 7;
-  const int64_t bj = blockIdx.x % kblocks;
-  const int64_t bi = blockIdx.x / kblocks;
+  const int64_t bj = blk % kblocks;
+  const int64_t bi = blk / kblocks;
   const int t = threadIdx.x;
   const int r0 = t >> 4;
   const int col = (t & 15) * 8;
@@ -109,6 +107,34 @@ __global__ __launch_bounds__(256) void quant_w_128x128_kernel(const uint16_t* __
     *reinterpret_cast<uint2*>(q + row * k + bj * 128 + col) = out;
   }
   if (t == 0) s[bi * kblocks + bj] = sc;
+}
+
+__global__ __launch_bounds__(256) void quant_w_128x128_kernel(const uint16_t* __restrict__ w,
+                                                              int64_t n, int64_t k,
+                                                              uint8_t* __restrict__ q,
+                                                              float* __restrict__ s) {
+  __shared__ float wave_max[4];
+  quant_w_block(w, n, k, q, s, blockIdx.x, wave_max);
+}
+
+// Several weight matrices in one launch: block b belongs to the entry whose range of block
+// indices [first[i], first[i+1]) holds it.
+constexpr int kWGroupMax = PURO_W_GROUP_MAX;
+struct WGroup {
+  const uint16_t* w[kWGroupMax];
+  uint8_t* q[kWGroupMax];
+  float* s[kWGroupMax];
+  int64_t n[kWGroupMax], k[kWGroupMax];
+  int64_t first[kWGroupMax + 1];
+  int count;
+};
+
+__global__ __launch_bounds__(256) void quant_w_128x128_group_kernel(const WGroup g) {
+  __shared__ float wave_max[4];
+  const int64_t b = blockIdx.x;
+  int i = 0;
+  while (i + 1 < g.count && b >= g.first[i + 1]) ++i;
+  quant_w_block(g.w[i], g.n[i], g.k[i], g.q[i], g.s[i], b - g.first[i], wave_max);
 }
 
 // ------------------------------------------------------------------ transposed 1x128 groups
@@ -351,5 +377,39 @@ extern "C" puro_status puro_quant_dual_1x128(const void* x, int64_t rows, int64_
   hipLaunchKernelGGL(quant_dual_1x128_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(x), rows,
                      cols, static_cast<uint8_t*>(q), s, static_cast<uint8_t*>(qt), st);
+  return launch_status();
+}
+
+extern "C" puro_status puro_quant_w_128x128_group(const puro_w_item* items, int count,
+                                                  void* stream) {
+  if (count < 0 || count > kWGroupMax) return PURO_ERR_ARG;
+  if (count == 0) return PURO_OK;
+  if (items == nullptr) return PURO_ERR_NULL;
+  WGroup g = {};
+  int64_t blocks = 0;
+  int used = 0;
+  for (int i = 0; i < count; ++i) {
+    const puro_w_item& it = items[i];
+    if (!dim_ok(it.n) || !dim_ok(it.k)) return PURO_ERR_SHAPE;
+    const bool empty = it.n == 0 || it.k == 0;
+    PURO_TRY(check_ptr(it.w, empty));
+    PURO_TRY(check_ptr(it.q, empty));
+    PURO_TRY(check_ptr(it.s, empty));
+    if (empty) continue;
+    g.w[used] = static_cast<const uint16_t*>(it.w);
+    g.q[used] = static_cast<uint8_t*>(it.q);
+    g.s[used] = it.s;
+    g.n[used] = it.n;
+    g.k[used] = it.k;
+    g.first[used] = blocks;
+    blocks += (it.n / 128) * (it.k / 128);
+    ++used;
+  }
+  if (used == 0) return PURO_OK;
+  if (blocks > INT32_MAX) return PURO_ERR_SHAPE;
+  g.first[used] = blocks;
+  g.count = used;
+  hipLaunchKernelGGL(quant_w_128x128_group_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256),
+                     0, static_cast<hipStream_t>(stream), g);
   return launch_status();
 }

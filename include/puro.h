@@ -74,6 +74,24 @@ puro_status puro_quant_act_1x128(const void* x, int64_t rows, int64_t cols, void
 puro_status puro_quant_w_128x128(const void* w, int64_t n, int64_t k, void* q, float* s,
                                  void* stream);
 
+/* Up to PURO_W_GROUP_MAX weight matrices quantised as puro_quant_w_128x128 in one launch (e.g.
+ * every weight of a layer, whose bf16 masters all change at an optimiser step). Same outputs,
+ * bit for bit, as one puro_quant_w_128x128 call per entry.
+ *   items  host array of `count` entries (0 <= count <= PURO_W_GROUP_MAX), each with
+ *          w bf16 [n][k], q e4m3 [n][k], s fp32 [n/128][k/128] as in puro_quant_w_128x128;
+ *          entries with n or k = 0 are skipped
+ * Every entry is validated before anything is enqueued; the first failure's status is
+ * returned. count outside [0, PURO_W_GROUP_MAX] returns PURO_ERR_ARG. Outputs of different
+ * entries must not overlap each other or any input. */
+#define PURO_W_GROUP_MAX 8
+typedef struct {
+  const void* w;
+  int64_t n, k;
+  void* q;
+  float* s;
+} puro_w_item;
+puro_status puro_quant_w_128x128_group(const puro_w_item* items, int count, void* stream);
+
 /* Transposed 1x128 requantiser for the weight-gradient GEMM, whose reduction dimension is the
  * token dimension: groups of 128 consecutive ROWS of each column, requantised from bf16, and
  * written transposed so that every group is contiguous. Equals puro_quant_act_1x128 applied to

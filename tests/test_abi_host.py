@@ -81,6 +81,27 @@ def test_dual_quant_validation(L):
     assert f(None, 0, 128, None, None, None, None, None) == 0      # empty: nothing to do
 
 
+def test_w_group_validation(L):
+    from blockwise_fp8_gemm_x128_amd._lib import PuroWItem
+    f = L.puro_quant_w_128x128_group
+    items = (PuroWItem * 9)()
+    for i in range(9):
+        items[i] = PuroWItem(FAKE, 128, 256, FAKE, FAKE)
+    assert f(items, -1, None) == 5                         # count out of range
+    assert f(items, 9, None) == 5
+    assert f(None, 1, None) == 1                           # NULL item array
+    assert f(None, 0, None) == 0                           # nothing to do
+    items[1] = PuroWItem(FAKE, 128, 200, FAKE, FAKE)
+    assert f(items, 2, None) == 2                          # ragged entry
+    items[1] = PuroWItem(None, 128, 256, FAKE, FAKE)
+    assert f(items, 2, None) == 1                          # NULL input of an entry
+    items[1] = PuroWItem(FAKE, 128, 256, FAKE, MIS)
+    assert f(items, 2, None) == 3                          # misaligned scales
+    items[0] = PuroWItem(None, 0, 256, None, None)         # empty entries are skipped
+    items[1] = PuroWItem(None, 128, 0, None, None)
+    assert f(items, 2, None) == 0
+
+
 def test_gemm_validation(L):
     fwd, dgrad, wgrad = L.puro_fp8_gemm_fwd, L.puro_fp8_gemm_dgrad, L.puro_fp8_gemm_wgrad
     for f in (fwd, dgrad):

@@ -139,6 +139,19 @@ def test_outlier_stress(puro, oracle):
     assert np.all(s[tcols.numpy(), rows.numpy()] == 1.0)
 
 
+def test_weight_group(puro, oracle):
+    # the four weights of a Qwen3-1.7B-shaped layer plus an empty one, in one launch
+    ws = [synth.randn_bf16((N, K), synth.W_STD, synth.config_seed(5, li, synth.KIND_W))
+          for li, (_, K, N) in enumerate(synth.LINEARS)]
+    ws.insert(2, torch.empty((0, 256), dtype=torch.bfloat16))
+    say("quant weight group", [tuple(w.shape) for w in ws])
+    qs, ss = puro.puro_quant_w_128x128_group([w.cuda() for w in ws])
+    torch.cuda.synchronize()
+    for i, (w, q, s) in enumerate(zip(ws, qs, ss)):
+        oq, os_ = oracle.quant_w_128x128(bf16_np(w))
+        assert_same(q.cpu().numpy(), s.cpu().numpy(), oq, os_, f"group entry {i}")
+
+
 def test_empty(puro):
     x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
     q, s = puro.puro_quant_act_1x128(x)

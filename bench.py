@@ -242,11 +242,12 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n}))
 
 
-def gemm_source_digest() -> str:
-    """Digest of the GEMM kernel sources, to tell whether stored counters still apply."""
+def source_digest(kind: str) -> str:
+    """Digest of the kernel sources of a launch kind, to tell whether stored counters still
+    apply (GEMM kinds: gemm.hip; quantiser kinds: quant.hip; both with common.hpp)."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("gemm.hip", "common.hpp"):
+    for f in ("gemm.hip" if kind.startswith("gemm") else "quant.hip", "common.hpp"):
         with open(os.path.join(ROOT, "blockwise_fp8_gemm_x128_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -255,17 +256,17 @@ def gemm_source_digest() -> str:
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_qwen3_1p7b_linear_stack_M8192.txt")
 
 
-def stored_traffic(kernel_class: str):
-    """HBM bytes per launch of `kernel_class` from the committed FETCH_SIZE / WRITE_SIZE summary
-    (its `traffic-record:` line, counters already scaled by the copy-kernel factors), or None if
-    there is none or the GEMM sources changed since the counters were taken."""
+def stored_traffic(kind: str):
+    """Average HBM bytes per launch of a launch kind from the committed FETCH_SIZE / WRITE_SIZE
+    summary (its `traffic-record:` lines, counters already scaled by the copy-kernel factors),
+    or None if there is none or the kind's sources changed since the counters were taken."""
     try:
         with open(TRAFFIC_SUMMARY) as fh:
             recs = [json.loads(l.split(":", 1)[1]) for l in fh if l.startswith("traffic-record:")]
     except (OSError, ValueError):
         return None
     for t in recs:
-        if t.get("source_digest") == gemm_source_digest() and t.get("kernel_class") == kernel_class:
+        if t.get("kind") == kind and t.get("source_digest") == source_digest(kind):
             return 1024.0 * (t["fetch_kib_per_launch"] * t["fetch_factor"] +
                              t["write_kib_per_launch"] * t["write_factor"])
     return None
@@ -346,40 +347,44 @@ def main():
             gb = d["bytes"] / (d["ms"] * 1e-3) / 1e9
             ent.update({"gbps": gb, "frac_hbm_peak": gb / PEAK_HBM_GBPS})
         kernels[cls] = ent
-    roofline = None
-    if kernels:
-        dom = max(kernels, key=lambda c: kernels[c]["ms_per_step"])
-        k = kernels[dom]
-        if "tflops" in k:
-            roofline = {"bound": "mfma", "achieved": k["tflops"], "peak": PEAK_FP8_TFLOPS,
-                        "unit": "TFLOP/s", "frac": k["frac_fp8_peak"],
-                        "traffic": stored_traffic(dom),
-                        "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
-                                        "scaled by a plain copy kernel)",
-                        "kernel": dom,
-                        "avg_launch_us": k["avg_launch_us"],
-                        "gemm_source_digest": gemm_source_digest()}
-        else:
-            roofline = {"bound": "hbm", "achieved": k["gbps"], "peak": PEAK_HBM_GBPS,
-                        "unit": "GB/s", "frac": k["frac_hbm_peak"], "traffic": None,
-                        "kernel": dom}
-    gemm_ms = sum(v["ms_per_step"] for c, v in kernels.items() if c.startswith("gemm"))
     by_kind = {}
     for c, v in kernels.items():
         kind = c.split("[")[0]
-        e = by_kind.setdefault(kind, {"ms_per_step": 0.0, "flops": 0.0, "bytes": 0.0})
+        e = by_kind.setdefault(kind, {"ms_per_step": 0.0, "launches_per_step": 0})
         e["ms_per_step"] += v["ms_per_step"]
+        e["launches_per_step"] += v["launches_per_step"]
     for kind, e in by_kind.items():
         fl = sum(l[1] for l in stack.launches if l[0].split("[")[0] == kind)
         by = sum(l[2] for l in stack.launches if l[0].split("[")[0] == kind)
         secs = e["ms_per_step"] * 1e-3
+        e["avg_launch_us"] = 1e3 * e["ms_per_step"] / e["launches_per_step"]
         if fl:
             e["tflops"] = fl / secs / 1e12
             e["frac_fp8_peak"] = e["tflops"] / PEAK_FP8_TFLOPS
         else:
             e["gbps"] = by / secs / 1e9
             e["frac_hbm_peak"] = e["gbps"] / PEAK_HBM_GBPS
-        del e["flops"], e["bytes"]
+    # Dominant kernel: the launch kind (one kernel function per kind; its launches differ only
+    # in shape) with the most time per step. achieved = its algorithmic work per launch,
+    # averaged over its launches, / its average launch duration.
+    roofline = None
+    if by_kind:
+        dom = max(by_kind, key=lambda c: by_kind[c]["ms_per_step"])
+        k = by_kind[dom]
+        common = {"traffic": stored_traffic(dom),
+                  "traffic_unit": "HBM bytes per launch, averaged over the kind's launches "
+                                  "(rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a plain copy "
+                                  "kernel)",
+                  "kernel": dom, "avg_launch_us": k["avg_launch_us"],
+                  "launches_per_step": k["launches_per_step"],
+                  "source_digest": source_digest(dom)}
+        if "tflops" in k:
+            roofline = {"bound": "mfma", "achieved": k["tflops"], "peak": PEAK_FP8_TFLOPS,
+                        "unit": "TFLOP/s", "frac": k["frac_fp8_peak"], **common}
+        else:
+            roofline = {"bound": "hbm", "achieved": k["gbps"], "peak": PEAK_HBM_GBPS,
+                        "unit": "GB/s", "frac": k["frac_hbm_peak"], **common}
+    gemm_ms = sum(v["ms_per_step"] for c, v in kernels.items() if c.startswith("gemm"))
     quant_ms = sum(v["ms_per_step"] for c, v in kernels.items() if c.startswith("quant"))
     gemm_flops = sum(l[1] for l in stack.launches)
     quant_bytes = sum(l[2] for l in stack.launches)

@@ -56,10 +56,10 @@ def lib():
             L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
             L.oracle_e4m3_encode.restype = ctypes.c_uint8
             L.oracle_e4m3_encode_array.argtypes = [P, I64, P]
-            L.oracle_quant_group.argtypes = [P, I64, I64, P, I64, P]
+            L.oracle_quant_group.argtypes = [P, I64, I64, P, I64, P, ctypes.c_int]
             for name in ("oracle_quant_act_1x128", "oracle_quant_w_128x128",
                          "oracle_quant_transpose"):
-                getattr(L, name).argtypes = [P, I64, I64, P, P]
+                getattr(L, name).argtypes = [P, I64, I64, P, P, ctypes.c_int]
                 getattr(L, name).restype = None
             for name in ("oracle_gemm_fwd", "oracle_gemm_dgrad", "oracle_gemm_wgrad"):
                 getattr(L, name).argtypes = [P, P, P, P, I64, I64, I64, P, I64, P]
@@ -115,45 +115,46 @@ def e4m3_encode_array(t) -> np.ndarray:
     return out
 
 
-def quant_group(x) -> tuple[np.ndarray, float]:
-    """Quantise one group (any length) of bf16 bit patterns."""
+def quant_group(x, pow2: bool = False) -> tuple[np.ndarray, float]:
+    """Quantise one group (any length) of bf16 bit patterns. ``pow2`` selects power-of-two
+    scales (the smallest 2^e, e >= -127, with 448 * 2^e >= amax) instead of amax/448."""
     x = _u16(x).reshape(-1)
     q = np.empty(x.size, dtype=np.uint8)
     s = np.empty(1, dtype=np.float32)
-    lib().oracle_quant_group(_ptr(x), x.size, 1, _ptr(q), 1, _ptr(s))
+    lib().oracle_quant_group(_ptr(x), x.size, 1, _ptr(q), 1, _ptr(s), int(bool(pow2)))
     return q, float(s[0])
 
 
-def quant_act_1x128(x) -> tuple[np.ndarray, np.ndarray]:
+def quant_act_1x128(x, pow2: bool = False) -> tuple[np.ndarray, np.ndarray]:
     """x[rows, cols] bf16 -> (q[rows, cols] uint8, s[cols/128, rows] float32)."""
     x = _u16(x)
     rows, cols = x.shape
     assert cols % 128 == 0
     q = np.empty((rows, cols), dtype=np.uint8)
     s = np.empty((cols // 128, rows), dtype=np.float32)
-    lib().oracle_quant_act_1x128(_ptr(x), rows, cols, _ptr(q), _ptr(s))
+    lib().oracle_quant_act_1x128(_ptr(x), rows, cols, _ptr(q), _ptr(s), int(bool(pow2)))
     return q, s
 
 
-def quant_w_128x128(w) -> tuple[np.ndarray, np.ndarray]:
+def quant_w_128x128(w, pow2: bool = False) -> tuple[np.ndarray, np.ndarray]:
     """w[n, k] bf16 -> (q[n, k] uint8, s[n/128, k/128] float32)."""
     w = _u16(w)
     n, k = w.shape
     assert n % 128 == 0 and k % 128 == 0
     q = np.empty((n, k), dtype=np.uint8)
     s = np.empty((n // 128, k // 128), dtype=np.float32)
-    lib().oracle_quant_w_128x128(_ptr(w), n, k, _ptr(q), _ptr(s))
+    lib().oracle_quant_w_128x128(_ptr(w), n, k, _ptr(q), _ptr(s), int(bool(pow2)))
     return q, s
 
 
-def quant_transpose(x) -> tuple[np.ndarray, np.ndarray]:
+def quant_transpose(x, pow2: bool = False) -> tuple[np.ndarray, np.ndarray]:
     """x[rows, cols] bf16 -> (qt[cols, rows] uint8, st[rows/128, cols] float32)."""
     x = _u16(x)
     rows, cols = x.shape
     assert rows % 128 == 0
     qt = np.empty((cols, rows), dtype=np.uint8)
     st = np.empty((rows // 128, cols), dtype=np.float32)
-    lib().oracle_quant_transpose(_ptr(x), rows, cols, _ptr(qt), _ptr(st))
+    lib().oracle_quant_transpose(_ptr(x), rows, cols, _ptr(qt), _ptr(st), int(bool(pow2)))
     return qt, st
 
 

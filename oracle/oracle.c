@@ -85,44 +85,79 @@ void oracle_e4m3_encode_array(const float* t, int64_t n, uint8_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_encode(t[i]);
 }
 
+/* Scale of one group from its max magnitude amax, and the factor that maps the group onto the
+ * E4M3 range. Standard scales: s = amax/448 and r = 448/amax as single correctly-rounded binary32
+ * divisions. Power-of-two scales (a variant of this library, not of the pages): s = 2^e for the
+ * least integer e with 448 * 2^e >= amax, with e raised to -127 if it falls below (the least
+ * power of two an 8-bit biased exponent holds); the payload is then x * 2^-e, exact. An all-zero
+ * group has s = 1 in both modes. */
+typedef struct {
+  float scale;
+  float recip; /* standard mode */
+  int e;       /* power-of-two mode */
+} group_scale_t;
+
+static int pow2_exponent(float amax) {
+  int e;
+  (void)frexp((double)amax, &e); /* amax in [2^(e-1), 2^e) */
+  e -= 9;                        /* a start near the answer; the two loops make it exact */
+  while (ldexp(448.0, e) < (double)amax) ++e;
+  while (ldexp(448.0, e - 1) >= (double)amax) --e;
+  return e < -127 ? -127 : e;
+}
+
+static group_scale_t group_scale_of(float amax, int pow2) {
+  group_scale_t g = {1.0f, 1.0f, 0};
+  if (amax == 0.0f) return g;
+  if (pow2) {
+    g.e = pow2_exponent(amax);
+    g.scale = (float)ldexp(1.0, g.e);
+  } else {
+    g.scale = amax / 448.0f;
+    g.recip = 448.0f / amax;
+  }
+  return g;
+}
+
+/* The scaled value of one bf16 element, clamped to the E4M3 range, ready for encoding. */
+static float scaled_value(uint16_t x, const group_scale_t* g, int pow2) {
+  float t = pow2 ? (float)ldexp((double)oracle_bf16_to_f32(x), -g->e)
+                 : oracle_bf16_to_f32(x) * g->recip;
+  if (t > 448.0f) t = 448.0f;
+  if (t < -448.0f) t = -448.0f;
+  return t;
+}
+
 /* One quantisation group: `count` bf16 values at x[i*stride] -> q[i*qstride], scale *s.
- * amax = max |x|; s = amax/448 and r = 448/amax as single correctly-rounded binary32
- * divisions (s = r = 1 for an all-zero group); q = E4M3(clamp(x*r, -448, 448)). */
+ * amax = max |x|; scale as above; q = E4M3(clamp(x scaled, -448, 448)). */
 void oracle_quant_group(const uint16_t* x, int64_t count, int64_t stride, uint8_t* q,
-                        int64_t qstride, float* s) {
+                        int64_t qstride, float* s, int pow2) {
   float amax = 0.0f;
   for (int64_t i = 0; i < count; ++i) {
     float v = fabsf(oracle_bf16_to_f32(x[i * stride]));
     if (v > amax) amax = v;
   }
-  float scale = 1.0f, recip = 1.0f;
-  if (amax != 0.0f) {
-    scale = amax / 448.0f;
-    recip = 448.0f / amax;
-  }
-  for (int64_t i = 0; i < count; ++i) {
-    float t = oracle_bf16_to_f32(x[i * stride]) * recip;
-    if (t > 448.0f) t = 448.0f;
-    if (t < -448.0f) t = -448.0f;
-    q[i * qstride] = oracle_e4m3_encode(t);
-  }
-  *s = scale;
+  group_scale_t g = group_scale_of(amax, pow2);
+  for (int64_t i = 0; i < count; ++i)
+    q[i * qstride] = oracle_e4m3_encode(scaled_value(x[i * stride], &g, pow2));
+  *s = g.scale;
 }
 
 /* Activations and their gradients: groups of 128 consecutive elements of a row (the row's
  * reduction dimension). Scale grid is chunk-major: s[c/128][r]. */
 void oracle_quant_act_1x128(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q,
-                            float* s) {
+                            float* s, int pow2) {
   int64_t chunks = cols / 128;
 #pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < rows; ++r)
     for (int64_t c = 0; c < chunks; ++c)
       oracle_quant_group(x + r * cols + c * 128, 128, 1, q + r * cols + c * 128, 1,
-                         s + c * rows + r);
+                         s + c * rows + r, pow2);
 }
 
 /* Weights: one scale per 128x128 block, gathered row by row of the block. */
-void oracle_quant_w_128x128(const uint16_t* w, int64_t n, int64_t k, uint8_t* q, float* s) {
+void oracle_quant_w_128x128(const uint16_t* w, int64_t n, int64_t k, uint8_t* q, float* s,
+                            int pow2) {
   int64_t nb = n / 128, kb = k / 128;
 #pragma omp parallel for schedule(static)
   for (int64_t b = 0; b < nb * kb; ++b) {
@@ -133,20 +168,13 @@ void oracle_quant_w_128x128(const uint16_t* w, int64_t n, int64_t k, uint8_t* q,
         float v = fabsf(oracle_bf16_to_f32(w[(bi * 128 + i) * k + bj * 128 + j]));
         if (v > amax) amax = v;
       }
-    float scale = 1.0f, recip = 1.0f;
-    if (amax != 0.0f) {
-      scale = amax / 448.0f;
-      recip = 448.0f / amax;
-    }
+    group_scale_t g = group_scale_of(amax, pow2);
     for (int64_t i = 0; i < 128; ++i)
       for (int64_t j = 0; j < 128; ++j) {
         int64_t idx = (bi * 128 + i) * k + bj * 128 + j;
-        float t = oracle_bf16_to_f32(w[idx]) * recip;
-        if (t > 448.0f) t = 448.0f;
-        if (t < -448.0f) t = -448.0f;
-        q[idx] = oracle_e4m3_encode(t);
+        q[idx] = oracle_e4m3_encode(scaled_value(w[idx], &g, pow2));
       }
-    s[bi * kb + bj] = scale;
+    s[bi * kb + bj] = g.scale;
   }
 }
 
@@ -154,13 +182,13 @@ void oracle_quant_w_128x128(const uint16_t* w, int64_t n, int64_t k, uint8_t* q,
  * so groups run down a column (128 consecutive rows). The result is stored transposed so that
  * each group is contiguous: qt[c][r], st[r/128][c]. Requantised from the bf16 source. */
 void oracle_quant_transpose(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* qt,
-                            float* st) {
+                            float* st, int pow2) {
   int64_t chunks = rows / 128;
 #pragma omp parallel for schedule(static)
   for (int64_t c = 0; c < cols; ++c)
     for (int64_t mb = 0; mb < chunks; ++mb)
       oracle_quant_group(x + mb * 128 * cols + c, 128, cols, qt + c * rows + mb * 128, 1,
-                         st + mb * cols + c);
+                         st + mb * cols + c, pow2);
 }
 
 /* E4M3 values are integer multiples of 2^-9 with magnitude <= 448, so v*512 is an integer

@@ -18,6 +18,12 @@
  * s = fl32(amax/448), payload q = E4M3_RNE(clamp(fl32(x * fl32(448/amax)), +-448)),
  * all-zero group -> s = 1, GEMM = sum over 128-chunks of sa*sb*(exact chunk dot product).
  *
+ * Power-of-two scale variant (pow2 = 1; this library's option, not stated on the pages): a
+ * nonzero group's scale is s = 2^e with e the least integer such that 448 * 2^e >= amax, raised
+ * to -127 if it is smaller; the payload is q = E4M3_RNE(x * 2^-e), the product exact. Such
+ * scales fit an 8-bit biased exponent (E8M0), which the matrix cores can apply themselves. The
+ * GEMM definitions below are unchanged: they take whatever scales they are given.
+ *
  * Layouts (all row-major, contiguous):
  *   bf16 tensors are passed as their raw uint16 bit patterns.
  *   quant_act_1x128 : x[rows][cols]          -> q[rows][cols], s[cols/128][rows]
@@ -42,11 +48,14 @@ double oracle_e4m3_decode(uint8_t code);
 uint8_t oracle_e4m3_encode(float t);
 void oracle_e4m3_encode_array(const float* t, int64_t n, uint8_t* out);
 void oracle_quant_group(const uint16_t* x, int64_t count, int64_t stride, uint8_t* q,
-                        int64_t qstride, float* s);
+                        int64_t qstride, float* s, int pow2);
 
-void oracle_quant_act_1x128(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q, float* s);
-void oracle_quant_w_128x128(const uint16_t* w, int64_t n, int64_t k, uint8_t* q, float* s);
-void oracle_quant_transpose(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* qt, float* st);
+void oracle_quant_act_1x128(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q, float* s,
+                            int pow2);
+void oracle_quant_w_128x128(const uint16_t* w, int64_t n, int64_t k, uint8_t* q, float* s,
+                            int pow2);
+void oracle_quant_transpose(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* qt, float* st,
+                            int pow2);
 
 void oracle_gemm_fwd(const uint8_t* xq, const float* sx, const uint8_t* wq, const float* sw,
                      int64_t M, int64_t N, int64_t K, const int64_t* rows, int64_t nrows,

@@ -28,9 +28,9 @@ def read_e4m3_hand():
     return rows
 
 
-def read_quant_hand():
+def read_quant_hand(name: str = "quant_hand.txt"):
     cases, cur = [], None
-    with open(os.path.join(GOLDEN, "quant_hand.txt")) as f:
+    with open(os.path.join(GOLDEN, name)) as f:
         for line in f:
             line = line.strip()
             if not line or line.startswith("#"):

@@ -8,7 +8,8 @@ down 6144->2048) at M = 8192 tokens (2 sequences of 4096):
 quant_dual_1x128 writes both 1x128 orientations from one read: X's transposed copy is made in
 the forward pass and kept for the weight gradient. With --unfused the step instead runs
 quant_act_1x128(X) forward and quant_act_1x128(dY), quant_transpose(dY), quant_transpose(X)
-backward (same results, 2 more bytes read per element of X and dY).
+backward (same results, 2 more bytes read per element of X and dY). With --pow2 every quantiser
+and GEMM is the library's power-of-two-scale (E8M0) variant.
 Every layer has its own seeded bf16 X, W, dY and fp32 dW buffers resident in HBM (~26 GB), so
 the 256 MB last-level cache cannot serve one layer's data to the next.
 
@@ -50,6 +51,9 @@ def parse():
                    help="time eager launches instead of one captured HIP graph per step")
     p.add_argument("--unfused", action="store_true",
                    help="separate quantiser launches per orientation instead of quant_dual_1x128")
+    p.add_argument("--pow2", action="store_true",
+                   help="power-of-two (E8M0) scales applied by the matrix cores: the library's "
+                        "_pow2 variant of every quantiser and GEMM")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     return p.parse_args()
@@ -58,7 +62,7 @@ def parse():
 class Stack:
     """Device buffers and pre-marshalled launches of the whole step."""
 
-    def __init__(self, layers: int, M: int, fused: bool = True):
+    def __init__(self, layers: int, M: int, fused: bool = True, pow2: bool = False):
         import torch
         from blockwise_fp8_gemm_x128_amd import binding as B
         from blockwise_fp8_gemm_x128_amd import synth
@@ -68,6 +72,11 @@ class Stack:
         self.launches = []  # (kernel class, flops, bytes, callable)
         shared = {}
         self.shared = shared  # intermediates reused across layers: keep them allocated
+
+        sfx = "_pow2" if pow2 else ""
+
+        def prep(name, *args):
+            return B.prepare(name + sfx, *args)
 
         def buf(key, shape, dtype):
             if key not in shared:
@@ -101,47 +110,47 @@ class Stack:
                 group_w.append(w)
                 group_q.append(wq)
                 group_s.append(sw)
-                g_fwd = (f"gemm_fwd[{name}]", f, 0.0,
-                         B.prepare("puro_fp8_gemm_fwd", xq, sx, wq, sw, y, M, N, K))
-                g_dgrad = (f"gemm_dgrad[{name}]", f, 0.0,
-                           B.prepare("puro_fp8_gemm_dgrad", dyq, sdy, wq, sw, dx, M, N, K))
+                g_fwd = (f"gemm_fwd{sfx}[{name}]", f, 0.0,
+                         prep("puro_fp8_gemm_fwd", xq, sx, wq, sw, y, M, N, K))
+                g_dgrad = (f"gemm_dgrad{sfx}[{name}]", f, 0.0,
+                           prep("puro_fp8_gemm_dgrad", dyq, sdy, wq, sw, dx, M, N, K))
                 if fused:
                     # X's transposed copy lives from this layer's forward to its backward
                     xtq = torch.empty((K, M), dtype=torch.uint8, device=dev)
                     sxt = torch.empty((M // 128, K), dtype=torch.float32, device=dev)
                     self.persist += [xtq, sxt]
-                    fwd += [("quant_dual_1x128", 0.0, M * K * B_DUAL,
-                             B.prepare("puro_quant_dual_1x128", x, M, K, xq, sx, xtq, sxt)),
+                    fwd += [("quant_dual_1x128" + sfx, 0.0, M * K * B_DUAL,
+                             prep("puro_quant_dual_1x128", x, M, K, xq, sx, xtq, sxt)),
                             g_fwd]
                     bwd.append([
-                        ("quant_dual_1x128", 0.0, M * N * B_DUAL,
-                         B.prepare("puro_quant_dual_1x128", dy, M, N, dyq, sdy, dytq, sdyt)),
+                        ("quant_dual_1x128" + sfx, 0.0, M * N * B_DUAL,
+                         prep("puro_quant_dual_1x128", dy, M, N, dyq, sdy, dytq, sdyt)),
                         g_dgrad,
-                        (f"gemm_wgrad[{name}]", f, 0.0,
-                         B.prepare("puro_fp8_gemm_wgrad", dytq, sdyt, xtq, sxt, dw, M, N, K, 0)),
+                        (f"gemm_wgrad{sfx}[{name}]", f, 0.0,
+                         prep("puro_fp8_gemm_wgrad", dytq, sdyt, xtq, sxt, dw, M, N, K, 0)),
                     ])
                 else:
                     xtq = buf(("xtq", M, K), (K, M), torch.uint8)
                     sxt = buf(("sxt", M, K), (M // 128, K), torch.float32)
-                    fwd += [("quant_act_1x128", 0.0, M * K * B_ACT,
-                             B.prepare("puro_quant_act_1x128", x, M, K, xq, sx)),
+                    fwd += [("quant_act_1x128" + sfx, 0.0, M * K * B_ACT,
+                             prep("puro_quant_act_1x128", x, M, K, xq, sx)),
                             g_fwd]
                     bwd.append([
-                        ("quant_act_1x128", 0.0, M * N * B_ACT,
-                         B.prepare("puro_quant_act_1x128", dy, M, N, dyq, sdy)),
+                        ("quant_act_1x128" + sfx, 0.0, M * N * B_ACT,
+                         prep("puro_quant_act_1x128", dy, M, N, dyq, sdy)),
                         g_dgrad,
-                        ("quant_transpose", 0.0, M * N * B_ACT,
-                         B.prepare("puro_quant_transpose", dy, M, N, dytq, sdyt)),
-                        ("quant_transpose", 0.0, M * K * B_ACT,
-                         B.prepare("puro_quant_transpose", x, M, K, xtq, sxt)),
-                        (f"gemm_wgrad[{name}]", f, 0.0,
-                         B.prepare("puro_fp8_gemm_wgrad", dytq, sdyt, xtq, sxt, dw, M, N, K, 0)),
+                        ("quant_transpose" + sfx, 0.0, M * N * B_ACT,
+                         prep("puro_quant_transpose", dy, M, N, dytq, sdyt)),
+                        ("quant_transpose" + sfx, 0.0, M * K * B_ACT,
+                         prep("puro_quant_transpose", x, M, K, xtq, sxt)),
+                        (f"gemm_wgrad{sfx}[{name}]", f, 0.0,
+                         prep("puro_fp8_gemm_wgrad", dytq, sdyt, xtq, sxt, dw, M, N, K, 0)),
                     ])
             # all four weights of the layer in one grouped launch
             items = B.w_group_items(group_w, group_q, group_s)
-            fwd[wslot] = ("quant_w_128x128", 0.0,
+            fwd[wslot] = ("quant_w_128x128" + sfx, 0.0,
                           sum(w.shape[0] * w.shape[1] for w in group_w) * B_W,
-                          B.prepare("puro_quant_w_128x128_group", items, len(group_w)))
+                          prep("puro_quant_w_128x128_group", items, len(group_w)))
         self.launches = fwd + [op for grp in reversed(bwd) for op in grp]
         self.graph = None
         self.flops = sum(l[1] for l in self.launches)
@@ -168,7 +177,8 @@ class Stack:
         self.graph.replay()
 
 
-def cpu_baseline(M: int, layers: int, rows_fwd: int = 64, rows_wgrad: int = 8):
+def cpu_baseline(M: int, layers: int, rows_fwd: int = 64, rows_wgrad: int = 8,
+                 pow2: bool = False):
     """The oracle on the host cores, on a bounded sample of one step: every quantiser of one
     layer at full size, and each GEMM of that layer on a seeded sample of output rows (all
     columns), extrapolated linearly to all rows and then to all layers."""
@@ -187,11 +197,11 @@ def cpu_baseline(M: int, layers: int, rows_fwd: int = 64, rows_wgrad: int = 8):
         w = u16(synth.randn_bf16((N, K), synth.W_STD, synth.stack_seed(0, li, synth.KIND_W)))
         dy = u16(synth.randn_bf16((M, N), synth.DY_STD, synth.stack_seed(0, li, synth.KIND_DY)))
         t0 = time.perf_counter()
-        wq, sw = oracle.quant_w_128x128(w)
-        xq, sx = oracle.quant_act_1x128(x)
-        dyq, sdy = oracle.quant_act_1x128(dy)
-        dytq, sdyt = oracle.quant_transpose(dy)
-        xtq, sxt = oracle.quant_transpose(x)
+        wq, sw = oracle.quant_w_128x128(w, pow2=pow2)
+        xq, sx = oracle.quant_act_1x128(x, pow2=pow2)
+        dyq, sdy = oracle.quant_act_1x128(dy, pow2=pow2)
+        dytq, sdyt = oracle.quant_transpose(dy, pow2=pow2)
+        xtq, sxt = oracle.quant_transpose(x, pow2=pow2)
         t1 = time.perf_counter()
         t_quant += t1 - t0
         rf = np.sort(rng.choice(M, rows_fwd, replace=False))
@@ -288,7 +298,7 @@ def main():
     M = M_TOKENS
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):  # every launch is bound to this stream when prepared
-        stack = Stack(args.layers, M, fused=not args.unfused)
+        stack = Stack(args.layers, M, fused=not args.unfused, pow2=args.pow2)
     torch.cuda.synchronize()
     with torch.cuda.stream(side):
         for _ in range(args.warmup):
@@ -409,7 +419,9 @@ def main():
                    "tokens_per_step": M, "seqs": M // 4096, "seq_len": 4096,
                    "layers": args.layers, "parallelism": "single GPU",
                    "quantisers": ("separate per orientation" if args.unfused else
-                                  "fused two-orientation 1x128 for X and dY")},
+                                  "fused two-orientation 1x128 for X and dY"),
+                   "scales": ("power of two (E8M0), applied by the matrix cores" if args.pow2
+                              else "fp32 amax/448, promoted in fp32 per 128-chunk")},
         "gemm_tflops": gemm_flops / (gemm_ms * 1e-3) / 1e12 if gemm_ms else None,
         "gemm_frac_fp8_peak": (gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS
                                if gemm_ms else None),
@@ -426,7 +438,7 @@ def main():
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(M, args.layers)
+        out["cpu_baseline"] = cpu_baseline(M, args.layers, pow2=args.pow2)
     print(json.dumps(out), flush=True)
 
 

@@ -14,6 +14,16 @@ __all__ = [
     "puro_fp8_gemm_fwd",
     "puro_fp8_gemm_dgrad",
     "puro_fp8_gemm_wgrad",
+    "puro_quant_dual_1x128",
+    "puro_quant_w_128x128_group",
+    "puro_quant_act_1x128_pow2",
+    "puro_quant_w_128x128_pow2",
+    "puro_quant_w_128x128_group_pow2",
+    "puro_quant_transpose_pow2",
+    "puro_quant_dual_1x128_pow2",
+    "puro_fp8_gemm_fwd_pow2",
+    "puro_fp8_gemm_dgrad_pow2",
+    "puro_fp8_gemm_wgrad_pow2",
 ]
 
 

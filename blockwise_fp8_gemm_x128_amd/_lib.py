@@ -35,6 +35,11 @@ SIGNATURES = {
     "puro_fp8_gemm_wgrad": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P],
                             ctypes.c_int),
 }
+# The power-of-two-scale variants take the same arguments as their standard counterparts.
+POW2_BASES = ("puro_quant_act_1x128", "puro_quant_w_128x128", "puro_quant_w_128x128_group",
+              "puro_quant_transpose", "puro_quant_dual_1x128", "puro_fp8_gemm_fwd",
+              "puro_fp8_gemm_dgrad", "puro_fp8_gemm_wgrad")
+SIGNATURES.update({b + "_pow2": SIGNATURES[b] for b in POW2_BASES})
 
 
 class PuroError(RuntimeError):

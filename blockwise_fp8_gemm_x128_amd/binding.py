@@ -44,27 +44,26 @@ def _out(t, name, dtype, shape, dev):
     return t
 
 
-def puro_quant_act_1x128(x: torch.Tensor, q=None, s=None):
+def puro_quant_act_1x128(x: torch.Tensor, q=None, s=None, _fn="puro_quant_act_1x128"):
     """x bf16 [rows, cols] -> (q uint8 E4M3 [rows, cols], s fp32 [cols/128, rows])."""
     dev = _dev(x)
     rows, cols = x.shape
     _need(x, "x", torch.bfloat16, (rows, cols), dev)
     q = _out(q, "q", FP8, (rows, cols), dev)
     s = _out(s, "s", torch.float32, (cols // 128, rows), dev)
-    check(lib().puro_quant_act_1x128(x.data_ptr(), rows, cols, q.data_ptr(), s.data_ptr(),
-                                     _stream(dev)))
+    check(getattr(lib(), _fn)(x.data_ptr(), rows, cols, q.data_ptr(), s.data_ptr(),
+                              _stream(dev)))
     return q, s
 
 
-def puro_quant_w_128x128(w: torch.Tensor, q=None, s=None):
+def puro_quant_w_128x128(w: torch.Tensor, q=None, s=None, _fn="puro_quant_w_128x128"):
     """w bf16 [n, k] -> (q uint8 E4M3 [n, k], s fp32 [n/128, k/128])."""
     dev = _dev(w)
     n, k = w.shape
     _need(w, "w", torch.bfloat16, (n, k), dev)
     q = _out(q, "q", FP8, (n, k), dev)
     s = _out(s, "s", torch.float32, (n // 128, k // 128), dev)
-    check(lib().puro_quant_w_128x128(w.data_ptr(), n, k, q.data_ptr(), s.data_ptr(),
-                                     _stream(dev)))
+    check(getattr(lib(), _fn)(w.data_ptr(), n, k, q.data_ptr(), s.data_ptr(), _stream(dev)))
     return q, s
 
 
@@ -85,7 +84,7 @@ def w_group_items(ws, qs, ss):
     return items
 
 
-def puro_quant_w_128x128_group(ws, qs=None, ss=None):
+def puro_quant_w_128x128_group(ws, qs=None, ss=None, _fn="puro_quant_w_128x128_group"):
     """Several bf16 weights [n, k] quantised in one launch -> (list of q, list of s), each as
     from puro_quant_w_128x128."""
     if not ws:
@@ -95,23 +94,24 @@ def puro_quant_w_128x128_group(ws, qs=None, ss=None):
     ss = ss or [torch.empty((w.shape[0] // 128, w.shape[1] // 128), dtype=torch.float32,
                             device=dev) for w in ws]
     items = w_group_items(ws, qs, ss)
-    check(lib().puro_quant_w_128x128_group(items, len(ws), _stream(dev)))
+    check(getattr(lib(), _fn)(items, len(ws), _stream(dev)))
     return qs, ss
 
 
-def puro_quant_transpose(x: torch.Tensor, qt=None, st=None):
+def puro_quant_transpose(x: torch.Tensor, qt=None, st=None, _fn="puro_quant_transpose"):
     """x bf16 [rows, cols] -> (qt uint8 E4M3 [cols, rows], st fp32 [rows/128, cols])."""
     dev = _dev(x)
     rows, cols = x.shape
     _need(x, "x", torch.bfloat16, (rows, cols), dev)
     qt = _out(qt, "qt", FP8, (cols, rows), dev)
     st = _out(st, "st", torch.float32, (rows // 128, cols), dev)
-    check(lib().puro_quant_transpose(x.data_ptr(), rows, cols, qt.data_ptr(), st.data_ptr(),
-                                     _stream(dev)))
+    check(getattr(lib(), _fn)(x.data_ptr(), rows, cols, qt.data_ptr(), st.data_ptr(),
+                              _stream(dev)))
     return qt, st
 
 
-def puro_quant_dual_1x128(x: torch.Tensor, q=None, s=None, qt=None, st=None):
+def puro_quant_dual_1x128(x: torch.Tensor, q=None, s=None, qt=None, st=None,
+                          _fn="puro_quant_dual_1x128"):
     """x bf16 [rows, cols] -> (q [rows, cols], s [cols/128, rows], qt [cols, rows],
     st [rows/128, cols]): the outputs of puro_quant_act_1x128 and puro_quant_transpose from one
     read of x."""
@@ -122,12 +122,12 @@ def puro_quant_dual_1x128(x: torch.Tensor, q=None, s=None, qt=None, st=None):
     s = _out(s, "s", torch.float32, (cols // 128, rows), dev)
     qt = _out(qt, "qt", FP8, (cols, rows), dev)
     st = _out(st, "st", torch.float32, (rows // 128, cols), dev)
-    check(lib().puro_quant_dual_1x128(x.data_ptr(), rows, cols, q.data_ptr(), s.data_ptr(),
-                                      qt.data_ptr(), st.data_ptr(), _stream(dev)))
+    check(getattr(lib(), _fn)(x.data_ptr(), rows, cols, q.data_ptr(), s.data_ptr(),
+                              qt.data_ptr(), st.data_ptr(), _stream(dev)))
     return q, s, qt, st
 
 
-def puro_fp8_gemm_fwd(xq, sx, wq, sw, y=None):
+def puro_fp8_gemm_fwd(xq, sx, wq, sw, y=None, _fn="puro_fp8_gemm_fwd"):
     """Y bf16 [M, N] from xq [M, K], sx [K/128, M], wq [N, K], sw [N/128, K/128]."""
     dev = _dev(xq)
     M, K = xq.shape
@@ -137,12 +137,12 @@ def puro_fp8_gemm_fwd(xq, sx, wq, sw, y=None):
     _need(wq, "wq", FP8, (N, K), dev)
     _need(sw, "sw", torch.float32, (N // 128, K // 128), dev)
     y = _out(y, "y", torch.bfloat16, (M, N), dev)
-    check(lib().puro_fp8_gemm_fwd(xq.data_ptr(), sx.data_ptr(), wq.data_ptr(), sw.data_ptr(),
-                                  y.data_ptr(), M, N, K, _stream(dev)))
+    check(getattr(lib(), _fn)(xq.data_ptr(), sx.data_ptr(), wq.data_ptr(), sw.data_ptr(),
+                              y.data_ptr(), M, N, K, _stream(dev)))
     return y
 
 
-def puro_fp8_gemm_dgrad(dyq, sdy, wq, sw, dx=None):
+def puro_fp8_gemm_dgrad(dyq, sdy, wq, sw, dx=None, _fn="puro_fp8_gemm_dgrad"):
     """dX bf16 [M, K] from dyq [M, N], sdy [N/128, M], wq [N, K], sw [N/128, K/128]."""
     dev = _dev(dyq)
     M, N = dyq.shape
@@ -152,12 +152,13 @@ def puro_fp8_gemm_dgrad(dyq, sdy, wq, sw, dx=None):
     _need(wq, "wq", FP8, (N, K), dev)
     _need(sw, "sw", torch.float32, (N // 128, K // 128), dev)
     dx = _out(dx, "dx", torch.bfloat16, (M, K), dev)
-    check(lib().puro_fp8_gemm_dgrad(dyq.data_ptr(), sdy.data_ptr(), wq.data_ptr(),
-                                    sw.data_ptr(), dx.data_ptr(), M, N, K, _stream(dev)))
+    check(getattr(lib(), _fn)(dyq.data_ptr(), sdy.data_ptr(), wq.data_ptr(), sw.data_ptr(),
+                              dx.data_ptr(), M, N, K, _stream(dev)))
     return dx
 
 
-def puro_fp8_gemm_wgrad(dytq, sdyt, xtq, sxt, dw=None, accumulate: bool = False):
+def puro_fp8_gemm_wgrad(dytq, sdyt, xtq, sxt, dw=None, accumulate: bool = False,
+                        _fn="puro_fp8_gemm_wgrad"):
     """dW fp32 [N, K] (= or +=) from dytq [N, M], sdyt [M/128, N], xtq [K, M], sxt [M/128, K]."""
     dev = _dev(dytq)
     N, M = dytq.shape
@@ -169,10 +170,31 @@ def puro_fp8_gemm_wgrad(dytq, sdyt, xtq, sxt, dw=None, accumulate: bool = False)
     if accumulate and dw is None:
         raise PuroError("accumulate=True needs an existing dw")
     dw = _out(dw, "dw", torch.float32, (N, K), dev)
-    check(lib().puro_fp8_gemm_wgrad(dytq.data_ptr(), sdyt.data_ptr(), xtq.data_ptr(),
-                                    sxt.data_ptr(), dw.data_ptr(), M, N, K,
-                                    1 if accumulate else 0, _stream(dev)))
+    check(getattr(lib(), _fn)(dytq.data_ptr(), sdyt.data_ptr(), xtq.data_ptr(),
+                              sxt.data_ptr(), dw.data_ptr(), M, N, K, 1 if accumulate else 0,
+                              _stream(dev)))
     return dw
+
+
+def _pow2_variant(base):
+    name = base.__name__ + "_pow2"
+
+    def f(*args, **kwargs):
+        return base(*args, _fn=name, **kwargs)
+
+    f.__name__ = name
+    f.__doc__ = (base.__doc__ or "") + "\n\n    Power-of-two scales (the library's E8M0 variant)."
+    return f
+
+
+puro_quant_act_1x128_pow2 = _pow2_variant(puro_quant_act_1x128)
+puro_quant_w_128x128_pow2 = _pow2_variant(puro_quant_w_128x128)
+puro_quant_w_128x128_group_pow2 = _pow2_variant(puro_quant_w_128x128_group)
+puro_quant_transpose_pow2 = _pow2_variant(puro_quant_transpose)
+puro_quant_dual_1x128_pow2 = _pow2_variant(puro_quant_dual_1x128)
+puro_fp8_gemm_fwd_pow2 = _pow2_variant(puro_fp8_gemm_fwd)
+puro_fp8_gemm_dgrad_pow2 = _pow2_variant(puro_fp8_gemm_dgrad)
+puro_fp8_gemm_wgrad_pow2 = _pow2_variant(puro_fp8_gemm_wgrad)
 
 
 def prepare(name: str, *args):

@@ -71,4 +71,29 @@ __device__ __forceinline__ void group_scale(float amax, float& s, float& r) {
   }
 }
 
+// Power-of-two scale of a group: s = 2^e for the least integer e with 448 * 2^e >= amax, raised
+// to -127 when smaller, and r = 2^-e exactly, so x * r is exact; an all-zero group gets
+// s = r = 1. With amax = (1 + f) * 2^(E - 127) (E the biased exponent field, f the fraction)
+// and 448 = 1.75 * 2^8: e = E - 135 when 1 + f <= 1.75, else E - 134. A subnormal amax lands
+// far below -127 and is raised to it. Finite bf16 inputs keep e <= 120, so 2^-e is a normal
+// fp32; s = 2^-127 is the fp32 subnormal 0x00400000.
+__device__ __forceinline__ void group_scale_pow2(float amax, float& s, float& r) {
+  const uint32_t u = __float_as_uint(amax);
+  int e = static_cast<int>(u >> 23) - 135 + ((u & 0x7fffffu) > 0x600000u ? 1 : 0);
+  e = e < -127 ? -127 : e;
+  if (amax == 0.0f) e = 0;
+  s = e >= -126 ? __uint_as_float(static_cast<uint32_t>(e + 127) << 23)
+                : __uint_as_float(0x00400000u);
+  r = __uint_as_float(static_cast<uint32_t>(127 - e) << 23);
+}
+
+// The group scale rule a kernel is instantiated for.
+template <bool kPow2>
+__device__ __forceinline__ void scale_rule(float amax, float& s, float& r) {
+  if constexpr (kPow2)
+    group_scale_pow2(amax, s, r);
+  else
+    group_scale(amax, s, r);
+}
+
 }  // namespace puro

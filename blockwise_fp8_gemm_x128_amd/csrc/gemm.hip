@@ -57,9 +57,10 @@ constexpr int kChunk = 128;       // reduction chunk = quantisation group
 constexpr int kSlab = 128 * 128;  // bytes of one 128-row x 128-byte staged slab
 constexpr int kGroupRows = 8;     // tile-rows per band of the block order
 
-template <int kMode, int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+template <int kMode, int BM_, int BN_, int WAVES_M_, int WAVES_N_, bool kPow2_ = false>
 struct Cfg {
   static constexpr int mode = kMode;
+  static constexpr bool kPow2 = kPow2_;  // power-of-two scales, applied by the matrix cores
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int kWaves = WAVES_M * WAVES_N;
@@ -94,6 +95,16 @@ __device__ __forceinline__ int swz_rows(int row) { return ((row >> 2) & 1) | ((r
 __device__ __forceinline__ int swz_slab(int row) { return ((row >> 2) & 1) | ((row >> 4) & 6); }
 
 __device__ __forceinline__ int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
+
+// A 64-bit value that is the same in every lane, moved to scalar registers. The tile origin is
+// computed with 64-bit divisions that the compiler expands on the vector ALU; without this it
+// can lose track of the result being uniform and wrap every buffer load that uses it in a
+// loop over distinct lane values.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
 
 __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b) {
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -217,6 +228,7 @@ struct FragOffsets {
   int bt[4];   // reduction-major B, per nj
   int sa;      // this lane's A scale (row r of each 16-row block)
   int sb;      // this lane's 4 B scales (columns 4G..4G+3 of each 16-column block)
+  int sbr;     // power-of-two mode: this lane's B scale (column r of each 16-column block)
 
   __device__ __forceinline__ void init(int wm, int wn, int lane) {
     const int G = lane >> 4, r = lane & 15;
@@ -235,6 +247,7 @@ struct FragOffsets {
     }
     sa = C::kSAOff + (wm * C::WM + r) * 4;
     sb = C::kSBOff + (wn * C::WN + 4 * G) * 4;
+    sbr = C::kSBOff + (wn * C::WN + r) * 4;
   }
 };
 
@@ -359,6 +372,78 @@ __device__ __forceinline__ void compute_chunk(const lds_u8* stage, float sb_blk,
   chunk_step<C, 0>(stage, o, st, sb_blk, acc);
 }
 
+// ------------------------------------------------------------------ power-of-two scales
+// When every scale is a power of two, the matrix core applies them itself: the scaled FP8
+// instruction takes one 8-bit biased exponent (E8M0) per operand row and lane, multiplies each
+// 32-element reduction block of that row by it, and adds into the accumulator it is given. A
+// lane (G, r) supplies the scale of row r of its operand for reduction block G; since one scale
+// covers all 128 elements of a chunk, that is simply the scale of row r. The chunk's MI x NJ
+// instructions then accumulate straight into acc, with no promotion on the vector ALU.
+//
+// The E8M0 byte of a positive power-of-two fp32 scale is its exponent field, including
+// 2^-127 (fp32 subnormal 0x00400000, field 0, which E8M0 code 0 denotes).
+__device__ __forceinline__ int e8m0(float s) { return static_cast<int>(__float_as_uint(s) >> 23); }
+
+template <class C>
+struct Pow2State {
+  v8i bf[C::NJ];
+  int eb[C::NJ];
+  v8i af_cur, af_next;
+  int ea_cur, ea_next;
+};
+
+template <class C, int nj>
+__device__ __forceinline__ void load_bf_pow2(const lds_u8* stage, const FragOffsets<C>& o,
+                                             Pow2State<C>& st, int eb_blk) {
+  if constexpr (nj < C::NJ) {
+    st.bf[nj] = frag_b<C, nj>(stage, o);
+    if constexpr (C::kPerColScale)
+      st.eb[nj] = e8m0(*reinterpret_cast<const lds_f32*>(stage + o.sbr + 64 * nj));
+    else
+      st.eb[nj] = eb_blk;
+    load_bf_pow2<C, nj + 1>(stage, o, st, eb_blk);
+  }
+}
+
+// Tile k = mi * NJ + nj; the next row block's A fragment and scale are fetched at the start of
+// each row block, as in the promoted path.
+template <class C, int k>
+__device__ __forceinline__ void pow2_step(const lds_u8* stage, const FragOffsets<C>& o,
+                                          Pow2State<C>& st, v4f (&acc)[C::MI][C::NJ]) {
+  if constexpr (k < C::MI * C::NJ) {
+    constexpr int mi = k / C::NJ, nj = k % C::NJ;
+    if constexpr (nj == 0 && mi + 1 < C::MI) {
+      st.af_next = frag_a<C, mi + 1>(stage, o);
+      st.ea_next = e8m0(scale_a<C, mi + 1>(stage, o));
+    }
+    acc[mi][nj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+        st.bf[nj], st.af_cur, acc[mi][nj], 0, 0, 0, st.eb[nj], 0, st.ea_cur);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (nj == C::NJ - 1 && mi + 1 < C::MI) {
+      st.af_cur = st.af_next;
+      st.ea_cur = st.ea_next;
+    }
+    pow2_step<C, k + 1>(stage, o, st, acc);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void compute_chunk_pow2(const lds_u8* stage, float sb_blk,
+                                                   const FragOffsets<C>& o,
+                                                   v4f (&acc)[C::MI][C::NJ]) {
+  Pow2State<C> st;
+  load_bf_pow2<C, 0>(stage, o, st, e8m0(sb_blk));
+  st.af_cur = frag_a<C, 0>(stage, o);
+  st.ea_cur = e8m0(scale_a<C, 0>(stage, o));
+  pow2_step<C, 0>(stage, o, st, acc);
+  // Pin the accumulators at the end of the chunk: without this, IR-level sinking moves the
+  // chunk's instructions past the next barrier, keeping all its fragments live (spills).
+#pragma unroll
+  for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+    for (int nj = 0; nj < C::NJ; ++nj) asm volatile("" : "+v"(acc[mi][nj]));
+}
+
 template <class C>
 __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A,
                                           const float* __restrict__ sA,
@@ -376,7 +461,7 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A,
   const int64_t local = b - band * kGroupRows * tiles_j;
   const int64_t ti = band * kGroupRows + local % band_rows;
   const int64_t tj = local / band_rows;
-  const int64_t i0 = ti * C::BM, j0 = tj * C::BN;
+  const int64_t i0 = uniform64(ti * C::BM), j0 = uniform64(tj * C::BN);
 
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -421,7 +506,10 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A,
       ld.issue(nxt, c + 1);
       if (!C::kPerColScale) sb_next = ld.sb_block[(c + 1) * ld.sb_block_step];
     }
-    compute_chunk<C>(cur, sb, fo, acc);
+    if constexpr (C::kPow2)
+      compute_chunk_pow2<C>(cur, sb, fo, acc);
+    else
+      compute_chunk<C>(cur, sb, fo, acc);
   };
   int64_t c = 0;
   for (; c + 1 < nk; c += 2) {
@@ -470,6 +558,15 @@ using WgradSmall = Cfg<kWgrad, 128, 128, 2, 2>;
 // output is 512 tiles).
 using WgradWide = Cfg<kWgrad, 256, 192, 2, 4>;
 using WgradTall = Cfg<kWgrad, 192, 256, 2, 4>;
+// The same shapes with power-of-two scales.
+using FwdBigP2 = Cfg<kFwd, 256, 256, 2, 4, true>;
+using DgradBigP2 = Cfg<kDgrad, 256, 256, 2, 4, true>;
+using WgradBigP2 = Cfg<kWgrad, 256, 256, 2, 4, true>;
+using FwdSmallP2 = Cfg<kFwd, 128, 128, 2, 2, true>;
+using DgradSmallP2 = Cfg<kDgrad, 128, 128, 2, 2, true>;
+using WgradSmallP2 = Cfg<kWgrad, 128, 128, 2, 2, true>;
+using WgradWideP2 = Cfg<kWgrad, 256, 192, 2, 4, true>;
+using WgradTallP2 = Cfg<kWgrad, 192, 256, 2, 4, true>;
 
 #define PURO_GEMM_KERNEL(NAME, CFG)                                                        \
   __global__ __launch_bounds__(CFG::kThreads) void NAME(                                   \
@@ -490,6 +587,14 @@ PURO_GEMM_KERNEL(gemm_dgrad_128x128, DgradSmall)
 PURO_GEMM_KERNEL(gemm_wgrad_128x128, WgradSmall)
 PURO_GEMM_KERNEL(gemm_wgrad_256x192, WgradWide)
 PURO_GEMM_KERNEL(gemm_wgrad_192x256, WgradTall)
+PURO_GEMM_KERNEL(gemm_fwd_256x256_pow2, FwdBigP2)
+PURO_GEMM_KERNEL(gemm_dgrad_256x256_pow2, DgradBigP2)
+PURO_GEMM_KERNEL(gemm_wgrad_256x256_pow2, WgradBigP2)
+PURO_GEMM_KERNEL(gemm_fwd_128x128_pow2, FwdSmallP2)
+PURO_GEMM_KERNEL(gemm_dgrad_128x128_pow2, DgradSmallP2)
+PURO_GEMM_KERNEL(gemm_wgrad_128x128_pow2, WgradSmallP2)
+PURO_GEMM_KERNEL(gemm_wgrad_256x192_pow2, WgradWideP2)
+PURO_GEMM_KERNEL(gemm_wgrad_192x256_pow2, WgradTallP2)
 
 // Number of compute units the big tiles must at least fill once.
 constexpr int64_t kComputeUnits = 256;
@@ -559,14 +664,44 @@ puro_status launch(GemmKernel k, const void* A, const float* sA, const void* B, 
   return launch_status();
 }
 
-}  // namespace
-}  // namespace puro
+// Kernels of one scale rule.
+template <bool kPow2>
+struct Kernels;
+template <>
+struct Kernels<false> {
+  using FwdB = FwdBig;
+  using FwdS = FwdSmall;
+  using DgB = DgradBig;
+  using DgS = DgradSmall;
+  using WgB = WgradBig;
+  using WgS = WgradSmall;
+  using WgW = WgradWide;
+  using WgT = WgradTall;
+  static constexpr GemmKernel fwd_b = gemm_fwd_256x256, fwd_s = gemm_fwd_128x128;
+  static constexpr GemmKernel dg_b = gemm_dgrad_256x256, dg_s = gemm_dgrad_128x128;
+  static constexpr GemmKernel wg_b = gemm_wgrad_256x256, wg_s = gemm_wgrad_128x128;
+  static constexpr GemmKernel wg_w = gemm_wgrad_256x192, wg_t = gemm_wgrad_192x256;
+};
+template <>
+struct Kernels<true> {
+  using FwdB = FwdBigP2;
+  using FwdS = FwdSmallP2;
+  using DgB = DgradBigP2;
+  using DgS = DgradSmallP2;
+  using WgB = WgradBigP2;
+  using WgS = WgradSmallP2;
+  using WgW = WgradWideP2;
+  using WgT = WgradTallP2;
+  static constexpr GemmKernel fwd_b = gemm_fwd_256x256_pow2, fwd_s = gemm_fwd_128x128_pow2;
+  static constexpr GemmKernel dg_b = gemm_dgrad_256x256_pow2, dg_s = gemm_dgrad_128x128_pow2;
+  static constexpr GemmKernel wg_b = gemm_wgrad_256x256_pow2, wg_s = gemm_wgrad_128x128_pow2;
+  static constexpr GemmKernel wg_w = gemm_wgrad_256x192_pow2, wg_t = gemm_wgrad_192x256_pow2;
+};
 
-using namespace puro;
-
-extern "C" puro_status puro_fp8_gemm_fwd(const void* xq, const float* sx, const void* wq,
-                                         const float* sw, void* y, int64_t M, int64_t N,
-                                         int64_t K, void* stream) {
+template <bool kPow2>
+puro_status gemm_fwd(const void* xq, const float* sx, const void* wq, const float* sw, void* y,
+                     int64_t M, int64_t N, int64_t K, void* stream) {
+  using Ks = Kernels<kPow2>;
   if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return PURO_ERR_SHAPE;
   const bool out_empty = M == 0 || N == 0;
   const bool red_empty = out_empty || K == 0;
@@ -577,13 +712,14 @@ extern "C" puro_status puro_fp8_gemm_fwd(const void* xq, const float* sx, const 
   PURO_TRY(check_ptr(y, out_empty));
   if (out_empty) return PURO_OK;
   if (use_big_tiles(M, N))
-    return launch<FwdBig>(gemm_fwd_256x256, xq, sx, wq, sw, y, M, N, K, 0, stream);
-  return launch<FwdSmall>(gemm_fwd_128x128, xq, sx, wq, sw, y, M, N, K, 0, stream);
+    return launch<typename Ks::FwdB>(Ks::fwd_b, xq, sx, wq, sw, y, M, N, K, 0, stream);
+  return launch<typename Ks::FwdS>(Ks::fwd_s, xq, sx, wq, sw, y, M, N, K, 0, stream);
 }
 
-extern "C" puro_status puro_fp8_gemm_dgrad(const void* dyq, const float* sdy, const void* wq,
-                                           const float* sw, void* dx, int64_t M, int64_t N,
-                                           int64_t K, void* stream) {
+template <bool kPow2>
+puro_status gemm_dgrad(const void* dyq, const float* sdy, const void* wq, const float* sw,
+                       void* dx, int64_t M, int64_t N, int64_t K, void* stream) {
+  using Ks = Kernels<kPow2>;
   if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return PURO_ERR_SHAPE;
   const bool out_empty = M == 0 || K == 0;
   const bool red_empty = out_empty || N == 0;
@@ -594,13 +730,15 @@ extern "C" puro_status puro_fp8_gemm_dgrad(const void* dyq, const float* sdy, co
   PURO_TRY(check_ptr(dx, out_empty));
   if (out_empty) return PURO_OK;
   if (use_big_tiles(M, K))
-    return launch<DgradBig>(gemm_dgrad_256x256, dyq, sdy, wq, sw, dx, M, K, N, 0, stream);
-  return launch<DgradSmall>(gemm_dgrad_128x128, dyq, sdy, wq, sw, dx, M, K, N, 0, stream);
+    return launch<typename Ks::DgB>(Ks::dg_b, dyq, sdy, wq, sw, dx, M, K, N, 0, stream);
+  return launch<typename Ks::DgS>(Ks::dg_s, dyq, sdy, wq, sw, dx, M, K, N, 0, stream);
 }
 
-extern "C" puro_status puro_fp8_gemm_wgrad(const void* dytq, const float* sdyt, const void* xtq,
-                                           const float* sxt, float* dw, int64_t M, int64_t N,
-                                           int64_t K, int accumulate, void* stream) {
+template <bool kPow2>
+puro_status gemm_wgrad(const void* dytq, const float* sdyt, const void* xtq, const float* sxt,
+                       float* dw, int64_t M, int64_t N, int64_t K, int accumulate,
+                       void* stream) {
+  using Ks = Kernels<kPow2>;
   if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return PURO_ERR_SHAPE;
   if (accumulate != 0 && accumulate != 1) return PURO_ERR_ARG;
   const bool out_empty = N == 0 || K == 0;
@@ -613,16 +751,54 @@ extern "C" puro_status puro_fp8_gemm_wgrad(const void* dytq, const float* sdyt, 
   if (out_empty) return PURO_OK;
   switch (pick_wgrad_shape(N, K)) {
     case kW256x256:
-      return launch<WgradBig>(gemm_wgrad_256x256, dytq, sdyt, xtq, sxt, dw, N, K, M,
-                              accumulate, stream);
+      return launch<typename Ks::WgB>(Ks::wg_b, dytq, sdyt, xtq, sxt, dw, N, K, M, accumulate,
+                                      stream);
     case kW256x192:
-      return launch<WgradWide>(gemm_wgrad_256x192, dytq, sdyt, xtq, sxt, dw, N, K, M,
-                               accumulate, stream);
+      return launch<typename Ks::WgW>(Ks::wg_w, dytq, sdyt, xtq, sxt, dw, N, K, M, accumulate,
+                                      stream);
     case kW192x256:
-      return launch<WgradTall>(gemm_wgrad_192x256, dytq, sdyt, xtq, sxt, dw, N, K, M,
-                               accumulate, stream);
+      return launch<typename Ks::WgT>(Ks::wg_t, dytq, sdyt, xtq, sxt, dw, N, K, M, accumulate,
+                                      stream);
     default:
-      return launch<WgradSmall>(gemm_wgrad_128x128, dytq, sdyt, xtq, sxt, dw, N, K, M,
-                                accumulate, stream);
+      return launch<typename Ks::WgS>(Ks::wg_s, dytq, sdyt, xtq, sxt, dw, N, K, M, accumulate,
+                                      stream);
   }
+}
+
+}  // namespace
+}  // namespace puro
+
+using namespace puro;
+
+extern "C" puro_status puro_fp8_gemm_fwd(const void* xq, const float* sx, const void* wq,
+                                         const float* sw, void* y, int64_t M, int64_t N,
+                                         int64_t K, void* stream) {
+  return gemm_fwd<false>(xq, sx, wq, sw, y, M, N, K, stream);
+}
+extern "C" puro_status puro_fp8_gemm_dgrad(const void* dyq, const float* sdy, const void* wq,
+                                           const float* sw, void* dx, int64_t M, int64_t N,
+                                           int64_t K, void* stream) {
+  return gemm_dgrad<false>(dyq, sdy, wq, sw, dx, M, N, K, stream);
+}
+extern "C" puro_status puro_fp8_gemm_wgrad(const void* dytq, const float* sdyt, const void* xtq,
+                                           const float* sxt, float* dw, int64_t M, int64_t N,
+                                           int64_t K, int accumulate, void* stream) {
+  return gemm_wgrad<false>(dytq, sdyt, xtq, sxt, dw, M, N, K, accumulate, stream);
+}
+
+extern "C" puro_status puro_fp8_gemm_fwd_pow2(const void* xq, const float* sx, const void* wq,
+                                              const float* sw, void* y, int64_t M, int64_t N,
+                                              int64_t K, void* stream) {
+  return gemm_fwd<true>(xq, sx, wq, sw, y, M, N, K, stream);
+}
+extern "C" puro_status puro_fp8_gemm_dgrad_pow2(const void* dyq, const float* sdy, const void* wq,
+                                                const float* sw, void* dx, int64_t M, int64_t N,
+                                                int64_t K, void* stream) {
+  return gemm_dgrad<true>(dyq, sdy, wq, sw, dx, M, N, K, stream);
+}
+extern "C" puro_status puro_fp8_gemm_wgrad_pow2(const void* dytq, const float* sdyt,
+                                                const void* xtq, const float* sxt, float* dw,
+                                                int64_t M, int64_t N, int64_t K, int accumulate,
+                                                void* stream) {
+  return gemm_wgrad<true>(dytq, sdyt, xtq, sxt, dw, M, N, K, accumulate, stream);
 }

@@ -23,6 +23,7 @@ namespace {
 constexpr int kActPasses = 4;
 constexpr int kActRowsPerBlock = 16 * kActPasses;
 
+template <bool kPow2>
 __global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t* __restrict__ x,
                                                               int64_t rows, int64_t cols,
                                                               uint8_t* __restrict__ q,
@@ -50,7 +51,7 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t* __
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
     float sc, r;
-    group_scale(m, sc, r);
+    scale_rule<kPow2>(m, sc, r);
     uint2 out;
     out.x = e4m3x4(f[0] * r, f[1] * r, f[2] * r, f[3] * r);
     out.y = e4m3x4(f[4] * r, f[5] * r, f[6] * r, f[7] * r);
@@ -61,6 +62,7 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t* __
 
 // ------------------------------------------------------------------ 128x128 weight blocks
 // One 256-thread block per 128x128 block: 16 lanes cover a 256 B row, 8 passes of 16 rows.
+template <bool kPow2>
 __device__ __forceinline__ void quant_w_block(const uint16_t* __restrict__ w, int64_t n, int64_t k,
                                               uint8_t* __restrict__ q, float* __restrict__ s,
                                               int64_t blk, float* wave_max) {
@@ -95,7 +97,7 @@ __device__ __forceinline__ void quant_w_block(const uint16_t* __restrict__ w, in
   __syncthreads();
   m = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
   float sc, r;
-  group_scale(m, sc, r);
+  scale_rule<kPow2>(m, sc, r);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int64_t row = bi * 128 + r0 + 16 * i;
@@ -109,12 +111,13 @@ __device__ __forceinline__ void quant_w_block(const uint16_t* __restrict__ w, in
   if (t == 0) s[bi * kblocks + bj] = sc;
 }
 
+template <bool kPow2>
 __global__ __launch_bounds__(256) void quant_w_128x128_kernel(const uint16_t* __restrict__ w,
                                                               int64_t n, int64_t k,
                                                               uint8_t* __restrict__ q,
                                                               float* __restrict__ s) {
   __shared__ float wave_max[4];
-  quant_w_block(w, n, k, q, s, blockIdx.x, wave_max);
+  quant_w_block<kPow2>(w, n, k, q, s, blockIdx.x, wave_max);
 }
 
 // Several weight matrices in one launch: block b belongs to the entry whose range of block
@@ -129,12 +132,13 @@ struct WGroup {
   int count;
 };
 
+template <bool kPow2>
 __global__ __launch_bounds__(256) void quant_w_128x128_group_kernel(const WGroup g) {
   __shared__ float wave_max[4];
   const int64_t b = blockIdx.x;
   int i = 0;
   while (i + 1 < g.count && b >= g.first[i + 1]) ++i;
-  quant_w_block(g.w[i], g.n[i], g.k[i], g.q[i], g.s[i], b - g.first[i], wave_max);
+  quant_w_block<kPow2>(g.w[i], g.n[i], g.k[i], g.q[i], g.s[i], b - g.first[i], wave_max);
 }
 
 // ------------------------------------------------------------------ transposed 1x128 groups
@@ -145,6 +149,7 @@ __global__ __launch_bounds__(256) void quant_w_128x128_group_kernel(const WGroup
 // 128 output bytes are written by 8 lanes as one contiguous 128 B segment.
 constexpr int kTrPitch = 33;  // dwords per staged row (32 data + 1 pad)
 
+template <bool kPow2>
 __global__ __launch_bounds__(256) void quant_transpose_kernel(const uint16_t* __restrict__ x,
                                                               int64_t rows, int64_t cols,
                                                               uint8_t* __restrict__ qt,
@@ -191,8 +196,8 @@ __global__ __launch_bounds__(256) void quant_transpose_kernel(const uint16_t* __
     m1v = fmaxf(m1v, __shfl_xor(m1v, off, 64));
   }
   float s0, r0, s1, r1;
-  group_scale(m0v, s0, r0);
-  group_scale(m1v, s1, r1);
+  scale_rule<kPow2>(m0v, s0, r0);
+  scale_rule<kPow2>(m1v, s1, r1);
   uint4 o0, o1;
   o0.x = e4m3x4(bf16_lo(d[0]) * r0, bf16_lo(d[1]) * r0, bf16_lo(d[2]) * r0, bf16_lo(d[3]) * r0);
   o0.y = e4m3x4(bf16_lo(d[4]) * r0, bf16_lo(d[5]) * r0, bf16_lo(d[6]) * r0, bf16_lo(d[7]) * r0);
@@ -221,6 +226,7 @@ __global__ __launch_bounds__(256) void quant_transpose_kernel(const uint16_t* __
 // rounds of 32.
 constexpr int kDualPitch = 65;  // dwords per staged row (64 data + 1 pad)
 
+template <bool kPow2>
 __global__ __launch_bounds__(256) void quant_dual_1x128_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, uint8_t* __restrict__ q,
     float* __restrict__ s, uint8_t* __restrict__ qt, float* __restrict__ st) {
@@ -253,7 +259,7 @@ __global__ __launch_bounds__(256) void quant_dual_1x128_kernel(
 #pragma unroll
       for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
       float sc, rc;
-      group_scale(m, sc, rc);
+      scale_rule<kPow2>(m, sc, rc);
       uint2 out;
       out.x = e4m3x4(f[0] * rc, f[1] * rc, f[2] * rc, f[3] * rc);
       out.y = e4m3x4(f[4] * rc, f[5] * rc, f[6] * rc, f[7] * rc);
@@ -283,8 +289,8 @@ __global__ __launch_bounds__(256) void quant_dual_1x128_kernel(
       m1v = fmaxf(m1v, __shfl_xor(m1v, off, 64));
     }
     float s0, r0, s1, r1;
-    group_scale(m0v, s0, r0);
-    group_scale(m1v, s1, r1);
+    scale_rule<kPow2>(m0v, s0, r0);
+    scale_rule<kPow2>(m1v, s1, r1);
     uint4 o0, o1;
     o0.x = e4m3x4(bf16_lo(d[0]) * r0, bf16_lo(d[1]) * r0, bf16_lo(d[2]) * r0,
                   bf16_lo(d[3]) * r0);
@@ -309,13 +315,12 @@ __global__ __launch_bounds__(256) void quant_dual_1x128_kernel(
   }
 }
 
-}  // namespace
-}  // namespace puro
-
-using namespace puro;
-
-extern "C" puro_status puro_quant_act_1x128(const void* x, int64_t rows, int64_t cols, void* q,
-                                            float* s, void* stream) {
+// ------------------------------------------------------------------ host side
+// Each entry point validates its arguments on the host, then launches the kernel instantiated
+// for its scale rule (amax/448, or the power of two at or above it).
+template <bool kPow2>
+puro_status quant_act_1x128(const void* x, int64_t rows, int64_t cols, void* q, float* s,
+                            void* stream) {
   if (!dim_ok(rows) || !dim_ok(cols)) return PURO_ERR_SHAPE;
   const bool empty = rows == 0 || cols == 0;
   PURO_TRY(check_ptr(x, empty));
@@ -324,14 +329,15 @@ extern "C" puro_status puro_quant_act_1x128(const void* x, int64_t rows, int64_t
   if (empty) return PURO_OK;
   const int64_t blocks = (rows / kActRowsPerBlock) * (cols / 128);
   if (blocks > INT32_MAX) return PURO_ERR_SHAPE;
-  hipLaunchKernelGGL(quant_act_1x128_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(x), rows,
-                     cols, static_cast<uint8_t*>(q), s);
+  hipLaunchKernelGGL(quant_act_1x128_kernel<kPow2>, dim3(static_cast<uint32_t>(blocks)),
+                     dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint16_t*>(x), rows, cols, static_cast<uint8_t*>(q), s);
   return launch_status();
 }
 
-extern "C" puro_status puro_quant_w_128x128(const void* w, int64_t n, int64_t k, void* q,
-                                            float* s, void* stream) {
+template <bool kPow2>
+puro_status quant_w_128x128(const void* w, int64_t n, int64_t k, void* q, float* s,
+                            void* stream) {
   if (!dim_ok(n) || !dim_ok(k)) return PURO_ERR_SHAPE;
   const bool empty = n == 0 || k == 0;
   PURO_TRY(check_ptr(w, empty));
@@ -340,14 +346,15 @@ extern "C" puro_status puro_quant_w_128x128(const void* w, int64_t n, int64_t k,
   if (empty) return PURO_OK;
   const int64_t blocks = (n / 128) * (k / 128);
   if (blocks > INT32_MAX) return PURO_ERR_SHAPE;
-  hipLaunchKernelGGL(quant_w_128x128_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(w), n, k,
-                     static_cast<uint8_t*>(q), s);
+  hipLaunchKernelGGL(quant_w_128x128_kernel<kPow2>, dim3(static_cast<uint32_t>(blocks)),
+                     dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint16_t*>(w), n, k, static_cast<uint8_t*>(q), s);
   return launch_status();
 }
 
-extern "C" puro_status puro_quant_transpose(const void* x, int64_t rows, int64_t cols, void* qt,
-                                            float* st, void* stream) {
+template <bool kPow2>
+puro_status quant_transpose(const void* x, int64_t rows, int64_t cols, void* qt, float* st,
+                            void* stream) {
   if (!dim_ok(rows) || !dim_ok(cols)) return PURO_ERR_SHAPE;
   const bool empty = rows == 0 || cols == 0;
   PURO_TRY(check_ptr(x, empty));
@@ -356,14 +363,16 @@ extern "C" puro_status puro_quant_transpose(const void* x, int64_t rows, int64_t
   if (empty) return PURO_OK;
   const int64_t blocks = (rows / 128) * (cols / 64);
   if (blocks > INT32_MAX) return PURO_ERR_SHAPE;
-  hipLaunchKernelGGL(quant_transpose_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(x), rows,
-                     cols, static_cast<uint8_t*>(qt), st);
+  hipLaunchKernelGGL(quant_transpose_kernel<kPow2>, dim3(static_cast<uint32_t>(blocks)),
+                     dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint16_t*>(x), rows, cols, static_cast<uint8_t*>(qt),
+                     st);
   return launch_status();
 }
 
-extern "C" puro_status puro_quant_dual_1x128(const void* x, int64_t rows, int64_t cols, void* q,
-                                             float* s, void* qt, float* st, void* stream) {
+template <bool kPow2>
+puro_status quant_dual_1x128(const void* x, int64_t rows, int64_t cols, void* q, float* s,
+                             void* qt, float* st, void* stream) {
   if (!dim_ok(rows) || !dim_ok(cols)) return PURO_ERR_SHAPE;
   const bool empty = rows == 0 || cols == 0;
   PURO_TRY(check_ptr(x, empty));
@@ -374,14 +383,15 @@ extern "C" puro_status puro_quant_dual_1x128(const void* x, int64_t rows, int64_
   if (empty) return PURO_OK;
   const int64_t blocks = (rows / 128) * (cols / 128);
   if (blocks > INT32_MAX) return PURO_ERR_SHAPE;
-  hipLaunchKernelGGL(quant_dual_1x128_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(x), rows,
-                     cols, static_cast<uint8_t*>(q), s, static_cast<uint8_t*>(qt), st);
+  hipLaunchKernelGGL(quant_dual_1x128_kernel<kPow2>, dim3(static_cast<uint32_t>(blocks)),
+                     dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint16_t*>(x), rows, cols, static_cast<uint8_t*>(q), s,
+                     static_cast<uint8_t*>(qt), st);
   return launch_status();
 }
 
-extern "C" puro_status puro_quant_w_128x128_group(const puro_w_item* items, int count,
-                                                  void* stream) {
+template <bool kPow2>
+puro_status quant_w_128x128_group(const puro_w_item* items, int count, void* stream) {
   if (count < 0 || count > kWGroupMax) return PURO_ERR_ARG;
   if (count == 0) return PURO_OK;
   if (items == nullptr) return PURO_ERR_NULL;
@@ -409,7 +419,55 @@ extern "C" puro_status puro_quant_w_128x128_group(const puro_w_item* items, int 
   if (blocks > INT32_MAX) return PURO_ERR_SHAPE;
   g.first[used] = blocks;
   g.count = used;
-  hipLaunchKernelGGL(quant_w_128x128_group_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256),
-                     0, static_cast<hipStream_t>(stream), g);
+  hipLaunchKernelGGL(quant_w_128x128_group_kernel<kPow2>, dim3(static_cast<uint32_t>(blocks)),
+                     dim3(256), 0, static_cast<hipStream_t>(stream), g);
   return launch_status();
+}
+
+}  // namespace
+}  // namespace puro
+
+using namespace puro;
+
+extern "C" puro_status puro_quant_act_1x128(const void* x, int64_t rows, int64_t cols, void* q,
+                                            float* s, void* stream) {
+  return quant_act_1x128<false>(x, rows, cols, q, s, stream);
+}
+extern "C" puro_status puro_quant_w_128x128(const void* w, int64_t n, int64_t k, void* q,
+                                            float* s, void* stream) {
+  return quant_w_128x128<false>(w, n, k, q, s, stream);
+}
+extern "C" puro_status puro_quant_transpose(const void* x, int64_t rows, int64_t cols, void* qt,
+                                            float* st, void* stream) {
+  return quant_transpose<false>(x, rows, cols, qt, st, stream);
+}
+extern "C" puro_status puro_quant_dual_1x128(const void* x, int64_t rows, int64_t cols, void* q,
+                                             float* s, void* qt, float* st, void* stream) {
+  return quant_dual_1x128<false>(x, rows, cols, q, s, qt, st, stream);
+}
+extern "C" puro_status puro_quant_w_128x128_group(const puro_w_item* items, int count,
+                                                  void* stream) {
+  return quant_w_128x128_group<false>(items, count, stream);
+}
+
+extern "C" puro_status puro_quant_act_1x128_pow2(const void* x, int64_t rows, int64_t cols,
+                                                 void* q, float* s, void* stream) {
+  return quant_act_1x128<true>(x, rows, cols, q, s, stream);
+}
+extern "C" puro_status puro_quant_w_128x128_pow2(const void* w, int64_t n, int64_t k, void* q,
+                                                 float* s, void* stream) {
+  return quant_w_128x128<true>(w, n, k, q, s, stream);
+}
+extern "C" puro_status puro_quant_transpose_pow2(const void* x, int64_t rows, int64_t cols,
+                                                 void* qt, float* st, void* stream) {
+  return quant_transpose<true>(x, rows, cols, qt, st, stream);
+}
+extern "C" puro_status puro_quant_dual_1x128_pow2(const void* x, int64_t rows, int64_t cols,
+                                                  void* q, float* s, void* qt, float* st,
+                                                  void* stream) {
+  return quant_dual_1x128<true>(x, rows, cols, q, s, qt, st, stream);
+}
+extern "C" puro_status puro_quant_w_128x128_group_pow2(const puro_w_item* items, int count,
+                                                       void* stream) {
+  return quant_w_128x128_group<true>(items, count, stream);
 }

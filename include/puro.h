@@ -141,6 +141,42 @@ puro_status puro_fp8_gemm_wgrad(const void* dytq, const float* sdyt, const void*
                                 const float* sxt, float* dw, int64_t M, int64_t N, int64_t K,
                                 int accumulate, void* stream);
 
+/* ---------------------------------------------------------------- power-of-two scales
+ * A variant of every entry point above with the same arguments, layouts and validation, whose
+ * scales are powers of two. This is an option of this library, not the pages' rule; the
+ * grouping (1x128 along the reduction dimension, 128x128 weight blocks) is theirs, as above.
+ *   scale    s = 2^e for the least integer e with 448 * 2^e >= amax, raised to -127 when it is
+ *            smaller (so tiny groups need no lower bound on amax); an all-zero group has s = 1;
+ *            s is stored as an ordinary fp32 value (2^-127 as the fp32 subnormal 0x00400000);
+ *   payload  q = E4M3_RNE(x * 2^-e), the product exact; |x * 2^-e| <= 448 needs no clamp;
+ *   GEMM     the same sums as above, with each operand's scale applied by the matrix cores as an
+ *            8-bit biased exponent (E8M0) and the chunk results accumulated by them in fp32.
+ * The _pow2 GEMMs read only the exponent field (bits 23-30) of each scale: they are meant for
+ * scales from the _pow2 quantisers, and take any other positive scale s as 2^floor(log2 s).
+ * Compared with amax/448 scales, a group's largest magnitude maps into (224, 448] instead of
+ * exactly onto 448: normal payloads keep their 3 mantissa bits, but up to one binade of E4M3
+ * range goes unused at the top, so small elements reach the subnormal range up to 2x sooner and
+ * amax itself is rounded like any other element. In exchange the GEMMs do no fp32 promotion
+ * work outside the matrix cores. */
+puro_status puro_quant_act_1x128_pow2(const void* x, int64_t rows, int64_t cols, void* q, float* s,
+                                      void* stream);
+puro_status puro_quant_w_128x128_pow2(const void* w, int64_t n, int64_t k, void* q, float* s,
+                                      void* stream);
+puro_status puro_quant_w_128x128_group_pow2(const puro_w_item* items, int count, void* stream);
+puro_status puro_quant_transpose_pow2(const void* x, int64_t rows, int64_t cols, void* qt,
+                                      float* st, void* stream);
+puro_status puro_quant_dual_1x128_pow2(const void* x, int64_t rows, int64_t cols, void* q,
+                                       float* s, void* qt, float* st, void* stream);
+puro_status puro_fp8_gemm_fwd_pow2(const void* xq, const float* sx, const void* wq,
+                                   const float* sw, void* y, int64_t M, int64_t N, int64_t K,
+                                   void* stream);
+puro_status puro_fp8_gemm_dgrad_pow2(const void* dyq, const float* sdy, const void* wq,
+                                     const float* sw, void* dx, int64_t M, int64_t N, int64_t K,
+                                     void* stream);
+puro_status puro_fp8_gemm_wgrad_pow2(const void* dytq, const float* sdyt, const void* xtq,
+                                     const float* sxt, float* dw, int64_t M, int64_t N, int64_t K,
+                                     int accumulate, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

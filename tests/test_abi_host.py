@@ -52,9 +52,23 @@ FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails va
 MIS = 0x10001   # misaligned
 
 
+POW2 = ["", "_pow2"]
+
+
+def test_every_entry_point_has_a_pow2_twin():
+    names = set(declared_functions())
+    bases = [n for n in names if n.startswith(("puro_quant_", "puro_fp8_gemm_"))
+             and not n.endswith("_pow2")]
+    assert len(bases) == 8
+    for n in bases:
+        assert n + "_pow2" in names, n
+
+
 @pytest.mark.parametrize("fn", ["puro_quant_act_1x128", "puro_quant_w_128x128",
                                 "puro_quant_transpose"])
-def test_quant_validation(L, fn):
+@pytest.mark.parametrize("sfx", POW2)
+def test_quant_validation(L, fn, sfx):
+    fn = fn + sfx
     f = getattr(L, fn)
     assert f(FAKE, 100, 128, FAKE, FAKE, None) == 2          # ragged rows
     assert f(FAKE, 128, 200, FAKE, FAKE, None) == 2          # ragged cols
@@ -69,8 +83,9 @@ def test_quant_validation(L, fn):
     assert f(None, 256, 0, None, None, None) == 0
 
 
-def test_dual_quant_validation(L):
-    f = L.puro_quant_dual_1x128
+@pytest.mark.parametrize("sfx", POW2)
+def test_dual_quant_validation(L, sfx):
+    f = getattr(L, "puro_quant_dual_1x128" + sfx)
     assert f(FAKE, 100, 128, FAKE, FAKE, FAKE, FAKE, None) == 2    # ragged rows
     assert f(FAKE, 128, 200, FAKE, FAKE, FAKE, FAKE, None) == 2    # ragged cols
     assert f(FAKE, 1 << 25, 128, FAKE, FAKE, FAKE, FAKE, None) == 2
@@ -81,9 +96,10 @@ def test_dual_quant_validation(L):
     assert f(None, 0, 128, None, None, None, None, None) == 0      # empty: nothing to do
 
 
-def test_w_group_validation(L):
+@pytest.mark.parametrize("sfx", POW2)
+def test_w_group_validation(L, sfx):
     from blockwise_fp8_gemm_x128_amd._lib import PuroWItem
-    f = L.puro_quant_w_128x128_group
+    f = getattr(L, "puro_quant_w_128x128_group" + sfx)
     items = (PuroWItem * 9)()
     for i in range(9):
         items[i] = PuroWItem(FAKE, 128, 256, FAKE, FAKE)
@@ -102,8 +118,9 @@ def test_w_group_validation(L):
     assert f(items, 2, None) == 0
 
 
-def test_gemm_validation(L):
-    fwd, dgrad, wgrad = L.puro_fp8_gemm_fwd, L.puro_fp8_gemm_dgrad, L.puro_fp8_gemm_wgrad
+@pytest.mark.parametrize("sfx", POW2)
+def test_gemm_validation(L, sfx):
+    fwd, dgrad, wgrad = (getattr(L, "puro_fp8_gemm_" + k + sfx) for k in ("fwd", "dgrad", "wgrad"))
     for f in (fwd, dgrad):
         assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 130, 128, 128, None) == 2
         assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 128, 128, 64, None) == 2

@@ -1,4 +1,5 @@
-"""GPU parity of the three GEMMs against the oracle, element by element, under the acceptance
+"""GPU parity of the three GEMMs (and their power-of-two-scale variants) against the oracle,
+element by element, under the acceptance
 rule |gpu - oracle| <= 2^-7 |oracle| + 1e-3 rms(oracle). The oracle quantises the same bf16
 inputs itself (its quantised operands are bit-identical to the GPU's, which the quantiser
 tests check separately) and computes exact chunk products with double accumulation.
@@ -40,47 +41,52 @@ def check(gpu, ref, what):
     return worst
 
 
-def run_fwd(puro, oracle, x, w, rows=None, what="fwd"):
+def fn(puro, name, pow2):
+    return getattr(puro, name + ("_pow2" if pow2 else ""))
+
+
+def run_fwd(puro, oracle, x, w, rows=None, what="fwd", pow2=False):
     M, K = x.shape
     N = w.shape[0]
-    say(what, "fwd M,N,K =", M, N, K)
-    xq, sx = puro.puro_quant_act_1x128(x.cuda())
-    wq, sw = puro.puro_quant_w_128x128(w.cuda())
-    y = puro.puro_fp8_gemm_fwd(xq, sx, wq, sw)
+    say(what, "fwd M,N,K =", M, N, K, "pow2" if pow2 else "")
+    xq, sx = fn(puro, "puro_quant_act_1x128", pow2)(x.cuda())
+    wq, sw = fn(puro, "puro_quant_w_128x128", pow2)(w.cuda())
+    y = fn(puro, "puro_fp8_gemm_fwd", pow2)(xq, sx, wq, sw)
     torch.cuda.synchronize()
-    oxq, osx = oracle.quant_act_1x128(bf16_np(x))
-    owq, osw = oracle.quant_w_128x128(bf16_np(w))
+    oxq, osx = oracle.quant_act_1x128(bf16_np(x), pow2=pow2)
+    owq, osw = oracle.quant_w_128x128(bf16_np(w), pow2=pow2)
     ref = oracle.gemm_fwd(oxq, osx, owq, osw, rows=rows)
     got = bf16_to_np64(y if rows is None else y[torch.as_tensor(rows).cuda()])
     return check(got, ref, what)
 
 
-def run_dgrad(puro, oracle, dy, w, rows=None, what="dgrad"):
+def run_dgrad(puro, oracle, dy, w, rows=None, what="dgrad", pow2=False):
     M, N = dy.shape
     K = w.shape[1]
-    say(what, "dgrad M,N,K =", M, N, K)
-    dyq, sdy = puro.puro_quant_act_1x128(dy.cuda())
-    wq, sw = puro.puro_quant_w_128x128(w.cuda())
-    dx = puro.puro_fp8_gemm_dgrad(dyq, sdy, wq, sw)
+    say(what, "dgrad M,N,K =", M, N, K, "pow2" if pow2 else "")
+    dyq, sdy = fn(puro, "puro_quant_act_1x128", pow2)(dy.cuda())
+    wq, sw = fn(puro, "puro_quant_w_128x128", pow2)(w.cuda())
+    dx = fn(puro, "puro_fp8_gemm_dgrad", pow2)(dyq, sdy, wq, sw)
     torch.cuda.synchronize()
-    odyq, osdy = oracle.quant_act_1x128(bf16_np(dy))
-    owq, osw = oracle.quant_w_128x128(bf16_np(w))
+    odyq, osdy = oracle.quant_act_1x128(bf16_np(dy), pow2=pow2)
+    owq, osw = oracle.quant_w_128x128(bf16_np(w), pow2=pow2)
     ref = oracle.gemm_dgrad(odyq, osdy, owq, osw, rows=rows)
     got = bf16_to_np64(dx if rows is None else dx[torch.as_tensor(rows).cuda()])
     return check(got, ref, what)
 
 
-def run_wgrad(puro, oracle, dy, x, rows=None, what="wgrad", dw0=None):
+def run_wgrad(puro, oracle, dy, x, rows=None, what="wgrad", dw0=None, pow2=False):
     M, N = dy.shape
     K = x.shape[1]
-    say(what, "wgrad M,N,K =", M, N, K)
-    dytq, sdyt = puro.puro_quant_transpose(dy.cuda())
-    xtq, sxt = puro.puro_quant_transpose(x.cuda())
+    say(what, "wgrad M,N,K =", M, N, K, "pow2" if pow2 else "")
+    dytq, sdyt = fn(puro, "puro_quant_transpose", pow2)(dy.cuda())
+    xtq, sxt = fn(puro, "puro_quant_transpose", pow2)(x.cuda())
     dw_in = None if dw0 is None else dw0.clone().cuda()
-    dw = puro.puro_fp8_gemm_wgrad(dytq, sdyt, xtq, sxt, dw=dw_in, accumulate=dw0 is not None)
+    dw = fn(puro, "puro_fp8_gemm_wgrad", pow2)(dytq, sdyt, xtq, sxt, dw=dw_in,
+                                               accumulate=dw0 is not None)
     torch.cuda.synchronize()
-    odytq, osdyt = oracle.quant_transpose(bf16_np(dy))
-    oxtq, osxt = oracle.quant_transpose(bf16_np(x))
+    odytq, osdyt = oracle.quant_transpose(bf16_np(dy), pow2=pow2)
+    oxtq, osxt = oracle.quant_transpose(bf16_np(x), pow2=pow2)
     ref = oracle.gemm_wgrad(odytq, osdyt, oxtq, osxt, rows=rows)
     if dw0 is not None:
         base = dw0.numpy().astype(np.float64)
@@ -91,31 +97,34 @@ def run_wgrad(puro, oracle, dy, x, rows=None, what="wgrad", dw0=None):
     return check(got, ref, what)
 
 
-def test_tiny_forward(puro, oracle):
+@pytest.mark.parametrize("pow2", [False, True])
+def test_tiny_forward(puro, oracle, pow2):
     x, w = synth.tiny_forward_inputs()
-    run_fwd(puro, oracle, x, w, what="tiny 256^3")
+    run_fwd(puro, oracle, x, w, what="tiny 256^3", pow2=pow2)
 
 
 SMALL = [(128, 128, 128), (384, 640, 384), (256, 384, 1152), (640, 256, 256), (1024, 768, 512)]
 
 
 @pytest.mark.parametrize("M,N,K", SMALL)
-def test_small_all_three(puro, oracle, M, N, K):
+@pytest.mark.parametrize("pow2", [False, True])
+def test_small_all_three(puro, oracle, M, N, K, pow2):
     seed = M * 7 + N * 3 + K
     x = synth.randn_bf16((M, K), 1.0, seed)
     w = synth.randn_bf16((N, K), 0.02, seed + 1)
     dy = synth.randn_bf16((M, N), 1e-3, seed + 2)
-    run_fwd(puro, oracle, x, w, what=f"fwd {M}x{N}x{K}")
-    run_dgrad(puro, oracle, dy, w, what=f"dgrad {M}x{N}x{K}")
-    run_wgrad(puro, oracle, dy, x, what=f"wgrad {M}x{N}x{K}")
+    run_fwd(puro, oracle, x, w, what=f"fwd {M}x{N}x{K}", pow2=pow2)
+    run_dgrad(puro, oracle, dy, w, what=f"dgrad {M}x{N}x{K}", pow2=pow2)
+    run_wgrad(puro, oracle, dy, x, what=f"wgrad {M}x{N}x{K}", pow2=pow2)
 
 
-def test_wgrad_accumulate(puro, oracle):
+@pytest.mark.parametrize("pow2", [False, True])
+def test_wgrad_accumulate(puro, oracle, pow2):
     M, N, K = 512, 256, 384
     x = synth.randn_bf16((M, K), 1.0, 71)
     dy = synth.randn_bf16((M, N), 1e-3, 72)
     dw0 = torch.randn((N, K), generator=torch.Generator().manual_seed(73)) * 1e-2
-    run_wgrad(puro, oracle, dy, x, dw0=dw0, what="wgrad accumulate")
+    run_wgrad(puro, oracle, dy, x, dw0=dw0, what="wgrad accumulate", pow2=pow2)
 
 
 # Weight-gradient outputs chosen so that each tile shape the library picks from is used on a
@@ -126,17 +135,18 @@ WGRAD_SHAPES = [(256, 128, 384), (256, 4096, 2048), (256, 2048, 4608), (256, 122
 
 
 @pytest.mark.parametrize("M,N,K", WGRAD_SHAPES)
-@pytest.mark.parametrize("acc", [False, True])
-def test_wgrad_tile_shapes(puro, oracle, M, N, K, acc):
+@pytest.mark.parametrize("acc,pow2", [(False, False), (True, False), (True, True)])
+def test_wgrad_tile_shapes(puro, oracle, M, N, K, acc, pow2):
     x = synth.randn_bf16((M, K), 1.0, 101 + N + K)
     dy = synth.randn_bf16((M, N), 1e-3, 102 + N + K)
     dw0 = (torch.randn((N, K), generator=torch.Generator().manual_seed(103)) * 1e-2
            if acc else None)
     run_wgrad(puro, oracle, dy, x, rows=sample_rows(N, 24, N + K), dw0=dw0,
-              what=f"wgrad tiles {M}x{N}x{K} acc={acc}")
+              what=f"wgrad tiles {M}x{N}x{K} acc={acc}", pow2=pow2)
 
 
-def test_big_tiles_with_ragged_edge(puro, oracle):
+@pytest.mark.parametrize("pow2", [False, True])
+def test_big_tiles_with_ragged_edge(puro, oracle, pow2):
     # 16512 = 64.5 x 256 rows: enough 256x256 tiles for the big-tile kernels, whose last tile
     # row is half outside the output; the sampled rows include that half tile.
     M, N, K = 16512, 1024, 256
@@ -144,9 +154,9 @@ def test_big_tiles_with_ragged_edge(puro, oracle):
     w = synth.randn_bf16((N, K), 0.02, 112)
     dy = synth.randn_bf16((M, N), 1e-3, 113)
     rows = np.unique(np.concatenate([sample_rows(M, 16, 114), np.arange(M - 130, M)]))
-    run_fwd(puro, oracle, x, w, rows=rows, what="fwd ragged big tiles")
+    run_fwd(puro, oracle, x, w, rows=rows, what="fwd ragged big tiles", pow2=pow2)
     w2 = synth.randn_bf16((N, 1024), 0.02, 115)
-    run_dgrad(puro, oracle, dy, w2, rows=rows, what="dgrad ragged big tiles")
+    run_dgrad(puro, oracle, dy, w2, rows=rows, what="dgrad ragged big tiles", pow2=pow2)
 
 
 def test_zero_reduction(puro):
@@ -173,7 +183,8 @@ def test_zero_reduction(puro):
     assert torch.count_nonzero(dw).item() == 0
 
 
-def test_zero_groups_and_scale_isolation(puro, oracle):
+@pytest.mark.parametrize("pow2", [False, True])
+def test_zero_groups_and_scale_isolation(puro, oracle, pow2):
     # rows with all-zero 1x128 tiles and one outlier block: exercises the s = 1 path inside GEMMs
     M, N, K = 384, 256, 512
     x = synth.randn_bf16((M, K), 1.0, 81).float()
@@ -184,7 +195,7 @@ def test_zero_groups_and_scale_isolation(puro, oracle):
     w = synth.randn_bf16((N, K), 0.02, 82).float()
     w[128:, 256:384] *= 50.0
     w = w.to(torch.bfloat16)
-    run_fwd(puro, oracle, x, w, what="fwd zero/outlier")
+    run_fwd(puro, oracle, x, w, what="fwd zero/outlier", pow2=pow2)
 
 
 def test_deterministic(puro):
@@ -217,10 +228,38 @@ def test_layer_fwd_bwd(puro, oracle, M, li):
     run_wgrad(puro, oracle, dy, x, rows=sample_rows(N, 16, li + 20), what=f"{name} wgrad M={M}")
 
 
-def test_outlier_fwd_bwd(puro, oracle):
+@pytest.mark.parametrize("pow2", [False, True])
+def test_outlier_fwd_bwd(puro, oracle, pow2):
     x, w, dy, _ = synth.outlier_inputs()
     M, K = x.shape
     N = w.shape[0]
-    run_fwd(puro, oracle, x, w, rows=sample_rows(M, 32, 1), what="outlier fwd")
-    run_dgrad(puro, oracle, dy, w, rows=sample_rows(M, 32, 2), what="outlier dgrad")
-    run_wgrad(puro, oracle, dy, x, rows=sample_rows(N, 16, 3), what="outlier wgrad")
+    run_fwd(puro, oracle, x, w, rows=sample_rows(M, 32, 1), what="outlier fwd", pow2=pow2)
+    run_dgrad(puro, oracle, dy, w, rows=sample_rows(M, 32, 2), what="outlier dgrad", pow2=pow2)
+    run_wgrad(puro, oracle, dy, x, rows=sample_rows(N, 16, 3), what="outlier wgrad", pow2=pow2)
+
+
+@pytest.mark.parametrize("li", range(4))
+def test_layer_fwd_bwd_pow2(puro, oracle, li):
+    name, K, N = synth.LINEARS[li]
+    M = 8192
+    x, w, dy = synth.linear_inputs(4, li, M, K, N)
+    run_fwd(puro, oracle, x, w, rows=sample_rows(M, 24, li), what=f"{name} fwd M={M}", pow2=True)
+    run_dgrad(puro, oracle, dy, w, rows=sample_rows(M, 24, li + 10), what=f"{name} dgrad M={M}",
+              pow2=True)
+    run_wgrad(puro, oracle, dy, x, rows=sample_rows(N, 16, li + 20), what=f"{name} wgrad M={M}",
+              pow2=True)
+
+
+def test_pow2_gemm_reads_only_scale_exponents(puro):
+    """The _pow2 GEMMs take each scale as an 8-bit biased exponent: scales given as 1.5 * 2^e
+    act as 2^e (documented behaviour for scales that did not come from the _pow2 quantisers)."""
+    say("pow2 exponent-only scales")
+    M, N, K = 256, 256, 256
+    x = synth.randn_bf16((M, K), 1.0, 121).cuda()
+    w = synth.randn_bf16((N, K), 0.02, 122).cuda()
+    xq, sx = puro.puro_quant_act_1x128_pow2(x)
+    wq, sw = puro.puro_quant_w_128x128_pow2(w)
+    y1 = puro.puro_fp8_gemm_fwd_pow2(xq, sx, wq, sw)
+    y2 = puro.puro_fp8_gemm_fwd_pow2(xq, sx * 1.5, wq, sw * 1.75)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))

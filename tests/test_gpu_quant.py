@@ -1,4 +1,5 @@
-"""GPU parity of the quantisers (including the fused two-orientation one): payload bytes and scales must equal the oracle's bit for
+"""GPU parity of the quantisers (including the fused two-orientation and grouped-weight ones,
+and the power-of-two-scale variants): payload bytes and scales must equal the oracle's bit for
 bit, on the tiny configuration, multi-tile and ragged shapes, special values, every bf16 value
 of the representable range, and the full-size Qwen3-1.7B layer shapes (M = 4096 and 16384) and
 the outlier stress inputs."""
@@ -19,20 +20,24 @@ def say(*a):
     sys.stdout.flush()
 
 
-def gpu_act(puro, x):
-    q, s = puro.puro_quant_act_1x128(x.cuda())
+def sfx(pow2):
+    return "_pow2" if pow2 else ""
+
+
+def gpu_act(puro, x, pow2=False):
+    q, s = getattr(puro, "puro_quant_act_1x128" + sfx(pow2))(x.cuda())
     torch.cuda.synchronize()
     return q.cpu().numpy(), s.cpu().numpy()
 
 
-def gpu_w(puro, w):
-    q, s = puro.puro_quant_w_128x128(w.cuda())
+def gpu_w(puro, w, pow2=False):
+    q, s = getattr(puro, "puro_quant_w_128x128" + sfx(pow2))(w.cuda())
     torch.cuda.synchronize()
     return q.cpu().numpy(), s.cpu().numpy()
 
 
-def gpu_tr(puro, x):
-    q, s = puro.puro_quant_transpose(x.cuda())
+def gpu_tr(puro, x, pow2=False):
+    q, s = getattr(puro, "puro_quant_transpose" + sfx(pow2))(x.cuda())
     torch.cuda.synchronize()
     return q.cpu().numpy(), s.cpu().numpy()
 
@@ -45,42 +50,46 @@ def assert_same(gq, gs, oq, os_, what):
     assert badv.size == 0, f"{what}: {len(badv)} scale mismatches, first {badv[:5].tolist()}"
 
 
-def check_all_three(puro, oracle, x, what, weight=True, transpose=True):
+def check_all_three(puro, oracle, x, what, weight=True, transpose=True, pow2=False):
+    what = what + (" pow2" if pow2 else "")
     say("quant", what, tuple(x.shape))
     xn = bf16_np(x)
-    gq, gs = gpu_act(puro, x)
-    oq, os_ = oracle.quant_act_1x128(xn)
+    gq, gs = gpu_act(puro, x, pow2)
+    oq, os_ = oracle.quant_act_1x128(xn, pow2=pow2)
     assert_same(gq, gs, oq, os_, what + " act")
     if weight:
-        gq, gs = gpu_w(puro, x)
-        wq, ws = oracle.quant_w_128x128(xn)
+        gq, gs = gpu_w(puro, x, pow2)
+        wq, ws = oracle.quant_w_128x128(xn, pow2=pow2)
         assert_same(gq, gs, wq, ws, what + " w")
     if transpose:
-        gq, gs = gpu_tr(puro, x)
-        tq, ts = oracle.quant_transpose(xn)
+        gq, gs = gpu_tr(puro, x, pow2)
+        tq, ts = oracle.quant_transpose(xn, pow2=pow2)
         assert_same(gq, gs, tq, ts, what + " transpose")
         # the fused quantiser: both orientations from one read, same bytes as the oracle's two
-        dq, ds, dqt, dst = puro.puro_quant_dual_1x128(x.cuda())
+        dq, ds, dqt, dst = getattr(puro, "puro_quant_dual_1x128" + sfx(pow2))(x.cuda())
         torch.cuda.synchronize()
         assert_same(dq.cpu().numpy(), ds.cpu().numpy(), oq, os_, what + " dual rows")
         assert_same(dqt.cpu().numpy(), dst.cpu().numpy(), tq, ts, what + " dual columns")
 
 
-def test_tiny_config(puro, oracle):
+@pytest.mark.parametrize("pow2", [False, True])
+def test_tiny_config(puro, oracle, pow2):
     x, w = synth.tiny_forward_inputs()
-    check_all_three(puro, oracle, x, "tiny X")
-    check_all_three(puro, oracle, w, "tiny W")
+    check_all_three(puro, oracle, x, "tiny X", pow2=pow2)
+    check_all_three(puro, oracle, w, "tiny W", pow2=pow2)
 
 
 @pytest.mark.parametrize("shape,std,seed", [
     ((128, 128), 1.0, 101), ((384, 640), 0.02, 102), ((256, 6144), 1e-3, 103),
     ((640, 128), 7.0, 104), ((1152, 384), 1e-30, 105)])
-def test_shapes(puro, oracle, shape, std, seed):
+@pytest.mark.parametrize("pow2", [False, True])
+def test_shapes(puro, oracle, shape, std, seed, pow2):
     x = synth.randn_bf16(shape, std, seed)
-    check_all_three(puro, oracle, x, f"randn std={std}")
+    check_all_three(puro, oracle, x, f"randn std={std}", pow2=pow2)
 
 
-def test_special_values(puro, oracle):
+@pytest.mark.parametrize("pow2", [False, True])
+def test_special_values(puro, oracle, pow2):
     rows = []
     z = np.zeros(128, np.float32)
     rows.append(z.copy())                                     # all +0
@@ -95,10 +104,11 @@ def test_special_values(puro, oracle):
     x = torch.tensor(np.stack(rows)).to(torch.bfloat16)
     pad = torch.zeros((128 - x.shape[0], 128), dtype=torch.bfloat16)
     x = torch.cat([x, pad])
-    check_all_three(puro, oracle, x, "special")
+    check_all_three(puro, oracle, x, "special", pow2=pow2)
 
 
-def test_every_bf16_value_through_unit_scale(puro, oracle):
+@pytest.mark.parametrize("pow2", [False, True])
+def test_every_bf16_value_through_unit_scale(puro, oracle, pow2):
     # groups of 127 bf16 values plus one 448: scale 1, so every representable-range bf16 value
     # reaches the E4M3 rounding unchanged (covers ties, subnormals, signed zeros)
     bits = np.arange(65536, dtype=np.uint32)
@@ -113,7 +123,7 @@ def test_every_bf16_value_through_unit_scale(puro, oracle):
     grid[:, :127] = flat.reshape(rows, 127)
     grid[:, 127] = 448.0
     x = torch.tensor(grid).to(torch.bfloat16)
-    check_all_three(puro, oracle, x, "all bf16", weight=False, transpose=False)
+    check_all_three(puro, oracle, x, "all bf16", weight=False, transpose=False, pow2=pow2)
 
 
 @pytest.mark.parametrize("M", [4096, 16384])
@@ -129,27 +139,40 @@ def test_layer_shapes(puro, oracle, M, li):
         check_all_three(puro, oracle, dy, f"{name} dY M={M}", weight=False, transpose=True)
 
 
-def test_outlier_stress(puro, oracle):
+@pytest.mark.parametrize("pow2", [False, True])
+def test_outlier_stress(puro, oracle, pow2):
     x, w, dy, picks = synth.outlier_inputs()
-    check_all_three(puro, oracle, x, "outlier X", weight=False, transpose=True)
-    check_all_three(puro, oracle, w, "outlier W", weight=True, transpose=False)
+    check_all_three(puro, oracle, x, "outlier X", weight=False, transpose=True, pow2=pow2)
+    check_all_three(puro, oracle, w, "outlier W", weight=True, transpose=False, pow2=pow2)
     # the zeroed tiles quantise to scale 1 and zero codes
-    q, s = gpu_act(puro, x)
+    q, s = gpu_act(puro, x, pow2)
     rows, tcols = picks["zero_tiles"]
     assert np.all(s[tcols.numpy(), rows.numpy()] == 1.0)
 
 
-def test_weight_group(puro, oracle):
+@pytest.mark.parametrize("pow2", [False, True])
+def test_weight_group(puro, oracle, pow2):
     # the four weights of a Qwen3-1.7B-shaped layer plus an empty one, in one launch
     ws = [synth.randn_bf16((N, K), synth.W_STD, synth.config_seed(5, li, synth.KIND_W))
           for li, (_, K, N) in enumerate(synth.LINEARS)]
     ws.insert(2, torch.empty((0, 256), dtype=torch.bfloat16))
     say("quant weight group", [tuple(w.shape) for w in ws])
-    qs, ss = puro.puro_quant_w_128x128_group([w.cuda() for w in ws])
+    qs, ss = getattr(puro, "puro_quant_w_128x128_group" + sfx(pow2))([w.cuda() for w in ws])
     torch.cuda.synchronize()
     for i, (w, q, s) in enumerate(zip(ws, qs, ss)):
-        oq, os_ = oracle.quant_w_128x128(bf16_np(w))
+        oq, os_ = oracle.quant_w_128x128(bf16_np(w), pow2=pow2)
         assert_same(q.cpu().numpy(), s.cpu().numpy(), oq, os_, f"group entry {i}")
+
+
+@pytest.mark.parametrize("li", range(4))
+def test_layer_shapes_pow2(puro, oracle, li):
+    name, K, N = synth.LINEARS[li]
+    x, w, dy = synth.linear_inputs(2, li, 16384, K, N)
+    check_all_three(puro, oracle, x, f"{name} X M=16384", weight=False, transpose=True,
+                    pow2=True)
+    check_all_three(puro, oracle, w, f"{name} W", weight=True, transpose=False, pow2=True)
+    check_all_three(puro, oracle, dy, f"{name} dY M=16384", weight=False, transpose=True,
+                    pow2=True)
 
 
 def test_empty(puro):
@@ -157,4 +180,6 @@ def test_empty(puro):
     q, s = puro.puro_quant_act_1x128(x)
     assert q.shape == (0, 256) and s.shape == (2, 0)
     q, s, qt, st = puro.puro_quant_dual_1x128(x)
+    assert q.shape == (0, 256) and s.shape == (2, 0) and qt.shape == (256, 0) and st.shape == (0, 256)
+    q, s, qt, st = puro.puro_quant_dual_1x128_pow2(x)
     assert q.shape == (0, 256) and s.shape == (2, 0) and qt.shape == (256, 0) and st.shape == (0, 256)

@@ -65,6 +65,13 @@ def lib():
                 getattr(L, name).argtypes = [P, P, P, P, I64, I64, I64, P, I64, P]
                 getattr(L, name).restype = None
             L.oracle_num_threads.restype = ctypes.c_int
+            D = ctypes.c_double
+            L.oracle_frobenius_norm.argtypes = [P, I64]
+            L.oracle_frobenius_norm.restype = D
+            L.oracle_hyperball_update.argtypes = [P, P, I64, D, D, P]
+            L.oracle_hyperball_update.restype = None
+            L.oracle_adamw.argtypes = [P, P, P, P, I64, D, D, D, D, D, I64, P, P, P]
+            L.oracle_adamw.restype = None
             _lib = L
     return _lib
 
@@ -224,3 +231,35 @@ def dequant_w(q, s) -> np.ndarray:
     """Exact dequantisation of a 128x128-blocked tensor."""
     v = e4m3_decode_array(q)
     return v * np.kron(s.astype(np.float64), np.ones((128, 128)))
+
+
+def _f32(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    assert a.dtype == np.float32, a.dtype
+    return a
+
+
+def frobenius_norm(w) -> float:
+    """sqrt(sum w^2) of an fp32 array, in binary64."""
+    w = _f32(w)
+    return float(lib().oracle_frobenius_norm(_ptr(w), w.size))
+
+
+def hyperball_update(w, u, lr: float, radius: float) -> np.ndarray:
+    """(w - lr*u) scaled to Frobenius norm `radius` (binary64, shape of w)."""
+    w, u = _f32(w), _f32(u)
+    assert w.shape == u.shape
+    out = np.empty(w.shape, dtype=np.float64)
+    lib().oracle_hyperball_update(_ptr(w), _ptr(u), w.size, float(lr), float(radius), _ptr(out))
+    return out
+
+
+def adamw(p, g, m, v, lr, beta1, beta2, eps, weight_decay, step):
+    """One AdamW step on fp32 state -> (p, m, v) in binary64."""
+    p, g, m, v = _f32(p), _f32(g), _f32(m), _f32(v)
+    assert p.shape == g.shape == m.shape == v.shape and step >= 1
+    outs = [np.empty(p.shape, dtype=np.float64) for _ in range(3)]
+    lib().oracle_adamw(_ptr(p), _ptr(g), _ptr(m), _ptr(v), p.size, float(lr), float(beta1),
+                       float(beta2), float(eps), float(weight_decay), int(step),
+                       *[_ptr(o) for o in outs])
+    return tuple(outs)

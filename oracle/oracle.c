@@ -279,3 +279,52 @@ void oracle_gemm_wgrad(const uint8_t* dytq, const float* sdyt, const uint8_t* xt
     }
   }
 }
+
+/* ---------------------------------------------------------------- optimizer step
+ * PuRo-2B news post (jj-blog-4lo.pages.dev), optimizer paragraph after the training-recipe
+ * paragraph: the optimizer (Hyperball) updates the matrices that are roughly scale-invariant
+ * and then scales each back to the Frobenius radius it had at initialisation, every step; the
+ * other parameters use AdamW. (daker.ai page, five-choices section: the update is kept inside a
+ * fixed radius.) The update direction of those matrices is not given on the pages; it is an
+ * input here. Everything below is binary64 on binary32 inputs, returned unrounded. */
+
+/* Frobenius norm sqrt(sum w_i^2); every square of a binary32 is exact in binary64. */
+double oracle_frobenius_norm(const float* w, int64_t n) {
+  double ss = 0.0;
+  for (int64_t i = 0; i < n; ++i) ss += (double)w[i] * (double)w[i];
+  return sqrt(ss);
+}
+
+/* One projected step: v = w - lr * u, then out = v * (radius / ||v||_F). A zero v is returned
+ * unchanged (it has no direction to scale). */
+void oracle_hyperball_update(const float* w, const float* u, int64_t n, double lr, double radius,
+                             double* out) {
+  double ss = 0.0;
+  for (int64_t i = 0; i < n; ++i) {
+    double v = (double)w[i] - lr * (double)u[i];
+    out[i] = v;
+    ss += v * v;
+  }
+  double f = ss > 0.0 ? radius / sqrt(ss) : 1.0;
+  for (int64_t i = 0; i < n; ++i) out[i] *= f;
+}
+
+/* AdamW with decoupled weight decay (Loshchilov and Hutter), step t >= 1:
+ *   p <- p * (1 - lr * wd)
+ *   m <- b1 * m + (1 - b1) * g          v <- b2 * v + (1 - b2) * g^2
+ *   p <- p - lr * (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps) */
+void oracle_adamw(const float* p, const float* g, const float* m, const float* v, int64_t n,
+                  double lr, double b1, double b2, double eps, double wd, int64_t step,
+                  double* p_out, double* m_out, double* v_out) {
+  double c1 = 1.0 - pow(b1, (double)step), c2 = 1.0 - pow(b2, (double)step);
+  for (int64_t i = 0; i < n; ++i) {
+    double gi = (double)g[i];
+    double mi = b1 * (double)m[i] + (1.0 - b1) * gi;
+    double vi = b2 * (double)v[i] + (1.0 - b2) * gi * gi;
+    double pi = (double)p[i] * (1.0 - lr * wd);
+    pi -= lr * (mi / c1) / (sqrt(vi / c2) + eps);
+    p_out[i] = pi;
+    m_out[i] = mi;
+    v_out[i] = vi;
+  }
+}

@@ -68,6 +68,16 @@ void oracle_gemm_wgrad(const uint8_t* dytq, const float* sdyt, const uint8_t* xt
                        int64_t nrows, double* out);
 int oracle_num_threads(void);
 
+/* Optimizer step (PuRo-2B news post, optimizer paragraph: scale-invariant matrices are scaled
+ * back to their initial Frobenius radius every step; AdamW for the other parameters). binary64
+ * arithmetic on binary32 inputs; results unrounded. */
+double oracle_frobenius_norm(const float* w, int64_t n);
+void oracle_hyperball_update(const float* w, const float* u, int64_t n, double lr, double radius,
+                             double* out);
+void oracle_adamw(const float* p, const float* g, const float* m, const float* v, int64_t n,
+                  double lr, double b1, double b2, double eps, double wd, int64_t step,
+                  double* p_out, double* m_out, double* v_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,6 +22,16 @@ class PuroWItem(ctypes.Structure):
     _fields_ = [("w", ctypes.c_void_p), ("n", ctypes.c_int64), ("k", ctypes.c_int64),
                 ("q", ctypes.c_void_p), ("s", ctypes.c_void_p)]
 
+class PuroAdamWParams(ctypes.Structure):
+    """puro_adamw_params: AdamW hyperparameters of one step."""
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("step", ctypes.c_int64)]
+
+
+OPT_MAX_BLOCKS = 2048  # PURO_OPT_MAX_BLOCKS
+OPT_WORKSPACE_BYTES = 8 * OPT_MAX_BLOCKS + 256  # PURO_OPT_WORKSPACE_BYTES
+
 SIGNATURES = {
     "puro_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "puro_abi_version": ([], ctypes.c_int),
@@ -35,6 +45,12 @@ SIGNATURES = {
     "puro_fp8_gemm_wgrad": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P],
                             ctypes.c_int),
 }
+SIGNATURES.update({
+    "puro_frobenius_norm": ([_P, _I64, _P, _P, _P], ctypes.c_int),
+    "puro_hyperball_step": ([_P, _P, _I64, ctypes.c_float, _P, _P, _P, _P], ctypes.c_int),
+    "puro_adamw_step": ([_P, _P, _P, _P, _I64, ctypes.POINTER(PuroAdamWParams), _P, _P],
+                        ctypes.c_int),
+})
 # The power-of-two-scale variants take the same arguments as their standard counterparts.
 POW2_BASES = ("puro_quant_act_1x128", "puro_quant_w_128x128", "puro_quant_w_128x128_group",
               "puro_quant_transpose", "puro_quant_dual_1x128", "puro_fp8_gemm_fwd",

@@ -7,9 +7,12 @@ computation runs in libpuro's HIP kernels; there is no other code path.
 """
 from __future__ import annotations
 
+import ctypes
+
 import torch
 
-from ._lib import W_GROUP_MAX, PuroError, PuroWItem, check, lib
+from ._lib import (OPT_WORKSPACE_BYTES, W_GROUP_MAX, PuroAdamWParams, PuroError, PuroWItem,
+                   check, lib)
 
 FP8 = torch.uint8  # E4M3 codes travel as raw bytes
 
@@ -174,6 +177,60 @@ def puro_fp8_gemm_wgrad(dytq, sdyt, xtq, sxt, dw=None, accumulate: bool = False,
                               sxt.data_ptr(), dw.data_ptr(), M, N, K, 1 if accumulate else 0,
                               _stream(dev)))
     return dw
+
+
+def optim_workspace(dev) -> torch.Tensor:
+    """Device workspace for the optimizer-step entry points (PURO_OPT_WORKSPACE_BYTES)."""
+    return torch.empty(OPT_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
+
+
+def puro_frobenius_norm(w: torch.Tensor, norm=None, workspace=None):
+    """||w||_F of an fp32 tensor -> fp32 device tensor of shape (1,)."""
+    dev = _dev(w)
+    _need(w, "w", torch.float32, tuple(w.shape), dev)
+    norm = _out(norm, "norm", torch.float32, (1,), dev)
+    ws = optim_workspace(dev) if workspace is None else workspace
+    check(lib().puro_frobenius_norm(w.data_ptr(), w.numel(), norm.data_ptr(), ws.data_ptr(),
+                                    _stream(dev)))
+    return norm
+
+
+def puro_hyperball_step(w: torch.Tensor, u: torch.Tensor, lr: float, radius: torch.Tensor,
+                        w_bf16=None, workspace=None):
+    """In place: w <- (w - lr*u) * radius / ||w - lr*u||_F; returns the bf16 copy of w."""
+    dev = _dev(w)
+    n = w.numel()
+    _need(w, "w", torch.float32, tuple(w.shape), dev)
+    _need(u, "u", torch.float32, tuple(w.shape), dev)
+    _need(radius, "radius", torch.float32, (1,), dev)
+    w_bf16 = _out(w_bf16, "w_bf16", torch.bfloat16, tuple(w.shape), dev)
+    ws = optim_workspace(dev) if workspace is None else workspace
+    check(lib().puro_hyperball_step(w.data_ptr(), u.data_ptr(), n, float(lr), radius.data_ptr(),
+                                    w_bf16.data_ptr(), ws.data_ptr(), _stream(dev)))
+    return w_bf16
+
+
+def adamw_params(lr, beta1, beta2, eps, weight_decay, step) -> PuroAdamWParams:
+    return PuroAdamWParams(lr, beta1, beta2, eps, weight_decay, int(step))
+
+
+def puro_adamw_step(p, g, m, v, lr, beta1, beta2, eps, weight_decay, step, p_bf16=None,
+                    want_bf16: bool = False):
+    """In place AdamW step on fp32 p, m, v with gradient g; returns the bf16 copy of p if
+    p_bf16 is given or want_bf16 is set, else None."""
+    dev = _dev(p)
+    shape = tuple(p.shape)
+    for t, name in ((p, "p"), (g, "g"), (m, "m"), (v, "v")):
+        _need(t, name, torch.float32, shape, dev)
+    if p_bf16 is None and want_bf16:
+        p_bf16 = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    if p_bf16 is not None:
+        _need(p_bf16, "p_bf16", torch.bfloat16, shape, dev)
+    hp = adamw_params(lr, beta1, beta2, eps, weight_decay, step)
+    check(lib().puro_adamw_step(p.data_ptr(), g.data_ptr(), m.data_ptr(), v.data_ptr(),
+                                p.numel(), ctypes.byref(hp),
+                                None if p_bf16 is None else p_bf16.data_ptr(), _stream(dev)))
+    return p_bf16
 
 
 def _pow2_variant(base):

@@ -1,0 +1,253 @@
+// Optimizer-step kernels for the fp32 master weights: the Frobenius-radius projection of the
+// updated linear-layer matrices, and AdamW for the other parameters.
+//
+// Method: PuRo-2B news post (jj-blog-4lo.pages.dev), optimizer paragraph after the
+// training-recipe paragraph — the matrices that are roughly scale-invariant get their update
+// and are then scaled back to the Frobenius radius they had at initialisation, every step; the
+// remaining parameters use AdamW. The masters stay fp32 (Paper walkthrough: Puro-2B, section
+// "Lever 2: use blockwise FP8 from step zero"), and each updated matrix is also written as the
+// bf16 copy the next step's 128x128 weight quantiser reads.
+//
+// All of it is HBM-bound streaming: 16 B per lane per access, grid-stride loops, and a
+// deterministic two-level reduction (fp64 per lane and per block, then one block summing the
+// block partials in index order) whose grid depends on the element count only, so results are
+// reproducible run to run and device to device.
+#include <math.h>
+
+#include "common.hpp"
+
+namespace puro {
+namespace {
+
+constexpr int kOptThreads = 256;
+constexpr int kOptMaxBlocks = PURO_OPT_MAX_BLOCKS;
+// workspace layout: [kOptMaxBlocks] double partial sums, then the scale factor (float)
+constexpr size_t kFactorOff = sizeof(double) * kOptMaxBlocks;
+static_assert(kFactorOff + 16 <= PURO_OPT_WORKSPACE_BYTES, "workspace too small");
+
+// Blocks of a reduction over n4 16-byte vectors: about four vectors per lane, at most
+// kOptMaxBlocks.
+inline int opt_blocks(int64_t n4) {
+  const int64_t per_block = int64_t(kOptThreads) * 4;
+  int64_t b = (n4 + per_block - 1) / per_block;
+  if (b < 1) b = 1;
+  if (b > kOptMaxBlocks) b = kOptMaxBlocks;
+  return static_cast<int>(b);
+}
+
+__device__ __forceinline__ double block_sum(double x, double* sh) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  const int t = threadIdx.x;
+  if ((t & 63) == 0) sh[t >> 6] = x;
+  __syncthreads();
+  return (sh[0] + sh[1]) + (sh[2] + sh[3]);
+}
+
+// Sum of squares, per block, of src (kUpdate false) or of v = src - lr*u, which is also
+// written to dst (kUpdate true; dst may be src: the update is done in place).
+template <bool kUpdate>
+__global__ __launch_bounds__(kOptThreads) void sumsq_kernel(const float* src,
+                                                            const float* __restrict__ u,
+                                                            float* dst, int64_t n4, float lr,
+                                                            double* __restrict__ partials) {
+  __shared__ double sh[kOptThreads / 64];
+  const float4* s4 = reinterpret_cast<const float4*>(src);
+  const float4* u4 = reinterpret_cast<const float4*>(u);
+  float4* d4 = reinterpret_cast<float4*>(dst);
+  double acc = 0.0;
+  for (int64_t i = int64_t(blockIdx.x) * kOptThreads + threadIdx.x; i < n4;
+       i += int64_t(gridDim.x) * kOptThreads) {
+    float4 a = s4[i];
+    if constexpr (kUpdate) {
+      const float4 b = u4[i];
+      a.x = fmaf(-lr, b.x, a.x);
+      a.y = fmaf(-lr, b.y, a.y);
+      a.z = fmaf(-lr, b.z, a.z);
+      a.w = fmaf(-lr, b.w, a.w);
+      d4[i] = a;
+    }
+    // each square of a binary32 is exact in binary64
+    acc += (double(a.x) * a.x + double(a.y) * a.y) + (double(a.z) * a.z + double(a.w) * a.w);
+  }
+  const double s = block_sum(acc, sh);
+  if (threadIdx.x == 0) partials[blockIdx.x] = s;
+}
+
+// One block: total of the partials in a fixed order, the norm, and the projection factor
+// radius / norm (1 for a zero matrix, which has no direction to scale).
+__global__ __launch_bounds__(kOptThreads) void finish_kernel(const double* __restrict__ partials,
+                                                             int count,
+                                                             const float* __restrict__ radius,
+                                                             float* __restrict__ factor,
+                                                             float* __restrict__ norm) {
+  __shared__ double sh[kOptThreads / 64];
+  double acc = 0.0;
+  for (int i = threadIdx.x; i < count; i += kOptThreads) acc += partials[i];
+  const double ss = block_sum(acc, sh);
+  if (threadIdx.x == 0) {
+    const double nrm = sqrt(ss);
+    if (norm) *norm = static_cast<float>(nrm);
+    if (factor) *factor = ss > 0.0 ? static_cast<float>(double(*radius) / nrm) : 1.0f;
+  }
+}
+
+__device__ __forceinline__ uint2 bf16x4(float4 a) {
+  uint2 o;
+  o.x = f32_to_bf16_rne(a.x) | (f32_to_bf16_rne(a.y) << 16);
+  o.y = f32_to_bf16_rne(a.z) | (f32_to_bf16_rne(a.w) << 16);
+  return o;
+}
+
+// w <- w * factor, and its bf16 copy.
+__global__ __launch_bounds__(kOptThreads) void scale_kernel(float* __restrict__ w, int64_t n4,
+                                                            const float* __restrict__ factor,
+                                                            uint16_t* __restrict__ wbf) {
+  const float f = *factor;
+  float4* w4 = reinterpret_cast<float4*>(w);
+  uint2* b4 = reinterpret_cast<uint2*>(wbf);
+  for (int64_t i = int64_t(blockIdx.x) * kOptThreads + threadIdx.x; i < n4;
+       i += int64_t(gridDim.x) * kOptThreads) {
+    float4 a = w4[i];
+    a.x *= f;
+    a.y *= f;
+    a.z *= f;
+    a.w *= f;
+    w4[i] = a;
+    b4[i] = bf16x4(a);
+  }
+}
+
+struct AdamWArgs {
+  float lr, b1, omb1, b2, omb2, eps, decay, c1, c2;  // decay = 1 - lr*wd; c = 1 - beta^t
+};
+
+__device__ __forceinline__ void adamw_one(float& p, float g, float& m, float& v,
+                                          const AdamWArgs& a) {
+  m = fmaf(a.b1, m, a.omb1 * g);
+  v = fmaf(a.b2, v, a.omb2 * (g * g));
+  const float mh = m / a.c1;
+  const float vh = v / a.c2;
+  p = p * a.decay - a.lr * (mh / (sqrtf(vh) + a.eps));
+}
+
+template <bool kBf16>
+__global__ __launch_bounds__(kOptThreads) void adamw_kernel(float* __restrict__ p,
+                                                            const float* __restrict__ g,
+                                                            float* __restrict__ m,
+                                                            float* __restrict__ v, int64_t n4,
+                                                            AdamWArgs a,
+                                                            uint16_t* __restrict__ pbf) {
+  float4* p4 = reinterpret_cast<float4*>(p);
+  const float4* g4 = reinterpret_cast<const float4*>(g);
+  float4* m4 = reinterpret_cast<float4*>(m);
+  float4* v4 = reinterpret_cast<float4*>(v);
+  for (int64_t i = int64_t(blockIdx.x) * kOptThreads + threadIdx.x; i < n4;
+       i += int64_t(gridDim.x) * kOptThreads) {
+    float4 pp = p4[i], mm = m4[i], vv = v4[i];
+    const float4 gg = g4[i];
+    adamw_one(pp.x, gg.x, mm.x, vv.x, a);
+    adamw_one(pp.y, gg.y, mm.y, vv.y, a);
+    adamw_one(pp.z, gg.z, mm.z, vv.z, a);
+    adamw_one(pp.w, gg.w, mm.w, vv.w, a);
+    p4[i] = pp;
+    m4[i] = mm;
+    v4[i] = vv;
+    if constexpr (kBf16) reinterpret_cast<uint2*>(pbf)[i] = bf16x4(pp);
+  }
+}
+
+// Elementwise kernels: enough blocks to fill the chip several times over, grid-stride beyond.
+inline int stream_blocks(int64_t n4) {
+  int64_t b = (n4 + kOptThreads - 1) / kOptThreads;
+  if (b < 1) b = 1;
+  if (b > 8192) b = 8192;
+  return static_cast<int>(b);
+}
+
+inline bool numel_ok(int64_t n) { return n >= 0 && n % 4 == 0 && n <= (int64_t(1) << 40); }
+
+}  // namespace
+}  // namespace puro
+
+using namespace puro;
+
+extern "C" puro_status puro_frobenius_norm(const float* w, int64_t numel, float* norm,
+                                           void* workspace, void* stream) {
+  if (!numel_ok(numel)) return PURO_ERR_SHAPE;
+  PURO_TRY(check_ptr(w, numel == 0));
+  if (norm == nullptr || workspace == nullptr) return PURO_ERR_NULL;
+  if (!aligned16(workspace) || (reinterpret_cast<uintptr_t>(norm) & 3u)) return PURO_ERR_ALIGN;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t n4 = numel / 4;
+  const int blocks = opt_blocks(n4);
+  double* partials = static_cast<double*>(workspace);
+  hipLaunchKernelGGL(sumsq_kernel<false>, dim3(blocks), dim3(kOptThreads), 0, s, w, nullptr,
+                     nullptr, n4, 0.0f, partials);
+  hipLaunchKernelGGL(finish_kernel, dim3(1), dim3(kOptThreads), 0, s, partials, blocks,
+                     nullptr, nullptr, norm);
+  return launch_status();
+}
+
+extern "C" puro_status puro_hyperball_step(float* w, const float* u, int64_t numel, float lr,
+                                           const float* radius, void* w_bf16, void* workspace,
+                                           void* stream) {
+  if (!numel_ok(numel)) return PURO_ERR_SHAPE;
+  if (!isfinite(lr)) return PURO_ERR_ARG;
+  const bool empty = numel == 0;
+  PURO_TRY(check_ptr(w, empty));
+  PURO_TRY(check_ptr(u, empty));
+  PURO_TRY(check_ptr(w_bf16, empty));
+  if (empty) return PURO_OK;
+  if (radius == nullptr || workspace == nullptr) return PURO_ERR_NULL;
+  if (!aligned16(workspace) || (reinterpret_cast<uintptr_t>(radius) & 3u)) return PURO_ERR_ALIGN;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t n4 = numel / 4;
+  const int blocks = opt_blocks(n4);
+  double* partials = static_cast<double*>(workspace);
+  float* factor = reinterpret_cast<float*>(static_cast<char*>(workspace) + kFactorOff);
+  hipLaunchKernelGGL(sumsq_kernel<true>, dim3(blocks), dim3(kOptThreads), 0, s, w, u, w, n4, lr,
+                     partials);
+  hipLaunchKernelGGL(finish_kernel, dim3(1), dim3(kOptThreads), 0, s, partials, blocks, radius,
+                     factor, nullptr);
+  hipLaunchKernelGGL(scale_kernel, dim3(stream_blocks(n4)), dim3(kOptThreads), 0, s, w, n4,
+                     factor, static_cast<uint16_t*>(w_bf16));
+  return launch_status();
+}
+
+extern "C" puro_status puro_adamw_step(float* p, const float* g, float* m, float* v,
+                                       int64_t numel, const puro_adamw_params* hp, void* p_bf16,
+                                       void* stream) {
+  if (!numel_ok(numel)) return PURO_ERR_SHAPE;
+  if (hp == nullptr) return PURO_ERR_NULL;
+  if (hp->step < 1 || !(hp->beta1 >= 0.0f && hp->beta1 < 1.0f) ||
+      !(hp->beta2 >= 0.0f && hp->beta2 < 1.0f) || !(hp->eps > 0.0f) || !isfinite(hp->lr) ||
+      !isfinite(hp->weight_decay))
+    return PURO_ERR_ARG;
+  const bool empty = numel == 0;
+  PURO_TRY(check_ptr(p, empty));
+  PURO_TRY(check_ptr(g, empty));
+  PURO_TRY(check_ptr(m, empty));
+  PURO_TRY(check_ptr(v, empty));
+  if (p_bf16 != nullptr && !aligned16(p_bf16)) return PURO_ERR_ALIGN;
+  if (empty) return PURO_OK;
+  AdamWArgs a;
+  a.lr = hp->lr;
+  a.b1 = hp->beta1;
+  a.omb1 = 1.0f - hp->beta1;
+  a.b2 = hp->beta2;
+  a.omb2 = 1.0f - hp->beta2;
+  a.eps = hp->eps;
+  a.decay = static_cast<float>(1.0 - double(hp->lr) * double(hp->weight_decay));
+  a.c1 = static_cast<float>(1.0 - pow(double(hp->beta1), double(hp->step)));
+  a.c2 = static_cast<float>(1.0 - pow(double(hp->beta2), double(hp->step)));
+  const int64_t n4 = numel / 4;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p_bf16)
+    hipLaunchKernelGGL(adamw_kernel<true>, dim3(stream_blocks(n4)), dim3(kOptThreads), 0, s, p,
+                       g, m, v, n4, a, static_cast<uint16_t*>(p_bf16));
+  else
+    hipLaunchKernelGGL(adamw_kernel<false>, dim3(stream_blocks(n4)), dim3(kOptThreads), 0, s, p,
+                       g, m, v, n4, a, nullptr);
+  return launch_status();
+}

@@ -141,6 +141,51 @@ puro_status puro_fp8_gemm_wgrad(const void* dytq, const float* sdyt, const void*
                                 const float* sxt, float* dw, int64_t M, int64_t N, int64_t K,
                                 int accumulate, void* stream);
 
+/* ---------------------------------------------------------------- optimizer step
+ * PuRo-2B news post (jj-blog-4lo.pages.dev), optimizer paragraph after the training-recipe
+ * paragraph: the roughly scale-invariant matrices (the linear-layer weights) are updated and
+ * then scaled back to the Frobenius radius they had at initialisation, every step; the other
+ * parameters use AdamW. The pages do not give the matrices' update direction (their MuonH
+ * orthogonalisation), so the projected step takes it as an input. Masters are fp32; the
+ * projected step also writes the bf16 copy that puro_quant_w_128x128 reads next.
+ *
+ * Conventions as above, plus: numel must be a multiple of 4 (PURO_ERR_SHAPE otherwise);
+ * `workspace` is caller-owned device memory of at least PURO_OPT_WORKSPACE_BYTES bytes,
+ * 16-byte aligned, used by one call at a time (calls sharing a workspace must be ordered on
+ * one stream). Reductions run in a fixed order set by numel alone, so results repeat exactly. */
+#define PURO_OPT_MAX_BLOCKS 2048
+#define PURO_OPT_WORKSPACE_BYTES (8 * PURO_OPT_MAX_BLOCKS + 256)
+
+/* Frobenius norm of w (fp32 [numel]), summed in fp64, written as fp32 to the device float
+ * *norm (e.g. a matrix's radius at initialisation). */
+puro_status puro_frobenius_norm(const float* w, int64_t numel, float* norm, void* workspace,
+                                void* stream);
+
+/* Projected step of one matrix, in place:
+ *   v = w - lr * u            (one fused multiply-add per element, fp32)
+ *   w = v * (radius / ||v||_F) (||v|| summed in fp64; the factor rounded once to fp32;
+ *                               a zero v is left unchanged)
+ *   w_bf16 = bf16_rne(w)
+ *   w       fp32 [numel], updated in place;  u fp32 [numel], the update direction
+ *   radius  DEVICE pointer to one fp32 (e.g. from puro_frobenius_norm at initialisation), so a
+ *           whole optimizer step can be captured without host round trips
+ *   w_bf16  bf16 [numel] (output) */
+puro_status puro_hyperball_step(float* w, const float* u, int64_t numel, float lr,
+                                const float* radius, void* w_bf16, void* workspace,
+                                void* stream);
+
+/* AdamW with decoupled weight decay (Loshchilov and Hutter), in place on fp32 state:
+ *   m = b1*m + (1-b1)*g;  v = b2*v + (1-b2)*g^2
+ *   p = p*(1 - lr*wd) - lr * (m/(1-b1^t)) / (sqrt(v/(1-b2^t)) + eps)
+ * p, g, m, v fp32 [numel]; p_bf16 (optional, NULL to skip) bf16 [numel] receives bf16_rne(p).
+ * hp is a host struct; step t >= 1, 0 <= beta < 1 and eps > 0, else PURO_ERR_ARG. */
+typedef struct {
+  float lr, beta1, beta2, eps, weight_decay;
+  int64_t step;
+} puro_adamw_params;
+puro_status puro_adamw_step(float* p, const float* g, float* m, float* v, int64_t numel,
+                            const puro_adamw_params* hp, void* p_bf16, void* stream);
+
 /* ---------------------------------------------------------------- power-of-two scales
  * A variant of every entry point above with the same arguments, layouts and validation, whose
  * scales are powers of two. This is an option of this library, not the pages' rule; the

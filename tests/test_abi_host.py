@@ -134,3 +134,36 @@ def test_gemm_validation(L, sfx):
     assert wgrad(FAKE, FAKE, FAKE, FAKE, FAKE, 128, 96, 128, 0, None) == 2
     assert wgrad(FAKE, FAKE, FAKE, FAKE, None, 128, 128, 128, 0, None) == 1
     assert wgrad(None, None, None, None, None, 128, 0, 128, 1, None) == 0
+
+
+def test_optim_validation(L):
+    from blockwise_fp8_gemm_x128_amd._lib import OPT_WORKSPACE_BYTES, PuroAdamWParams
+    assert OPT_WORKSPACE_BYTES == 8 * 2048 + 256
+    text = open(HEADER).read()
+    assert "#define PURO_OPT_MAX_BLOCKS 2048" in text
+    norm, hb, adamw = L.puro_frobenius_norm, L.puro_hyperball_step, L.puro_adamw_step
+    assert norm(FAKE, 6, FAKE, FAKE, None) == 2            # numel not a multiple of 4
+    assert norm(FAKE, -4, FAKE, FAKE, None) == 2
+    assert norm(None, 8, FAKE, FAKE, None) == 1
+    assert norm(FAKE, 8, None, FAKE, None) == 1            # NULL output
+    assert norm(FAKE, 8, FAKE, None, None) == 1            # NULL workspace
+    assert norm(FAKE, 8, FAKE, MIS, None) == 3             # misaligned workspace
+    assert hb(FAKE, FAKE, 6, 0.1, FAKE, FAKE, FAKE, None) == 2
+    assert hb(FAKE, None, 8, 0.1, FAKE, FAKE, FAKE, None) == 1
+    assert hb(FAKE, FAKE, 8, 0.1, None, FAKE, FAKE, None) == 1    # NULL radius
+    assert hb(FAKE, FAKE, 8, 0.1, FAKE, FAKE, None, None) == 1    # NULL workspace
+    assert hb(FAKE, FAKE, 8, 0.1, FAKE, MIS, FAKE, None) == 3     # misaligned bf16 output
+    assert hb(FAKE, FAKE, 8, float("nan"), FAKE, FAKE, FAKE, None) == 5
+    assert hb(None, None, 0, 0.1, None, None, None, None) == 0    # empty: nothing to do
+    ok = PuroAdamWParams(1e-3, 0.9, 0.95, 1e-8, 0.1, 1)
+    assert adamw(FAKE, FAKE, FAKE, FAKE, 6, ctypes.byref(ok), None, None) == 2
+    assert adamw(FAKE, FAKE, FAKE, FAKE, 8, None, None, None) == 1
+    assert adamw(FAKE, FAKE, None, FAKE, 8, ctypes.byref(ok), None, None) == 1
+    assert adamw(FAKE, FAKE, FAKE, FAKE, 8, ctypes.byref(ok), MIS, None) == 3
+    for bad in (PuroAdamWParams(1e-3, 0.9, 0.95, 1e-8, 0.1, 0),      # step 0
+                PuroAdamWParams(1e-3, 1.0, 0.95, 1e-8, 0.1, 1),      # beta1 = 1
+                PuroAdamWParams(1e-3, 0.9, -0.1, 1e-8, 0.1, 1),      # beta2 < 0
+                PuroAdamWParams(1e-3, 0.9, 0.95, 0.0, 0.1, 1),       # eps = 0
+                PuroAdamWParams(float("inf"), 0.9, 0.95, 1e-8, 0.1, 1)):
+        assert adamw(FAKE, FAKE, FAKE, FAKE, 8, ctypes.byref(bad), None, None) == 5
+    assert adamw(None, None, None, None, 0, ctypes.byref(ok), None, None) == 0

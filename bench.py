@@ -54,6 +54,8 @@ def parse():
     p.add_argument("--pow2", action="store_true",
                    help="power-of-two (E8M0) scales applied by the matrix cores: the library's "
                         "_pow2 variant of every quantiser and GEMM")
+    p.add_argument("--no-optim", action="store_true",
+                   help="skip the optimizer-step measurement")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     return p.parse_args()
@@ -84,6 +86,7 @@ class Stack:
             return shared[key]
 
         self.persist = []
+        self.weights = []
         fwd, bwd = [], []
         for layer in range(layers):
             group_w, group_q, group_s = [], [], []
@@ -106,6 +109,7 @@ class Stack:
                 dytq = buf(("dytq", M, N), (N, M), torch.uint8)
                 sdyt = buf(("sdyt", M, N), (M // 128, N), torch.float32)
                 self.persist += [x, w, dy, wq, sw, dw]
+                self.weights.append((w, dw))  # bf16 copy of the master, and its gradient
                 f = 2.0 * M * N * K
                 group_w.append(w)
                 group_q.append(wq)
@@ -235,6 +239,78 @@ def cpu_baseline(M: int, layers: int, rows_fwd: int = 64, rows_wgrad: int = 8,
         "step_s_extrapolated": step_s,
         "quant_s_per_layer": t_quant,
         "gemm_s_per_layer_extrapolated": t_gemm,
+    }
+
+
+# algorithmic bytes per element of the optimizer kernels
+B_HYPERBALL = 4 + 4 + 4 + 4 + 4 + 2   # read w, u; write v; read v; write w, w_bf16
+B_ADAMW = 4 * 4 + 3 * 4                # read p, g, m, v; write p, m, v
+ADAMW_STANDIN = 1 << 26                # elements of the AdamW measurement (stated size)
+
+
+def optimizer_bench(stack, steps: int):
+    """Optimizer step over the stack's 112 linear matrices, timed apart from the training step
+    (it runs once per global batch, not per micro-batch): fp32 masters made from the bf16
+    weights, their initial Frobenius radii, and each matrix's dW from the stack as the update
+    direction; each projected step also rewrites the bf16 weight the quantiser reads. Plus
+    AdamW on a stand-in fp32 parameter vector of ADAMW_STANDIN elements."""
+    import ctypes
+
+    import torch
+    from blockwise_fp8_gemm_x128_amd import binding as B
+
+    dev = torch.device("cuda:0")
+    ws = B.optim_workspace(dev)
+    masters, calls, numel = [], [], 0
+    for w, dw in stack.weights:
+        m = w.float()
+        r = B.puro_frobenius_norm(m, workspace=ws)
+        masters.append((m, r))
+        calls.append(B.prepare("puro_hyperball_step", m, dw, m.numel(), 1e-3, r, w, ws))
+        numel += m.numel()
+    torch.cuda.synchronize()
+    for call in calls:  # warm-up
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for e0, e1 in ev:
+        e0.record(stack.stream)
+        for call in calls:
+            call()
+        e1.record(stack.stream)
+    torch.cuda.synchronize()
+    ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / steps
+    gbps = numel * B_HYPERBALL / (ms * 1e-3) / 1e9
+
+    n = ADAMW_STANDIN
+    p, g, mm, vv = (torch.randn(n, device=dev) * 0.02 for _ in range(4))
+    vv = vv.abs()
+    call = B.prepare("puro_adamw_step", p, g, mm, vv, n,
+                     ctypes.byref(B.adamw_params(1e-3, 0.9, 0.95, 1e-8, 0.1, 1)),
+                     None)
+    call()
+    torch.cuda.synchronize()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(stack.stream)
+    for _ in range(steps):
+        call()
+    a1.record(stack.stream)
+    torch.cuda.synchronize()
+    ams = a0.elapsed_time(a1) / steps
+    agbps = n * B_ADAMW / (ams * 1e-3) / 1e9
+    del masters
+    return {
+        "projected_step": {"matrices": len(calls), "elements": numel,
+                           "ms_per_optimizer_step": ms, "gbps": gbps,
+                           "frac_hbm_peak": gbps / PEAK_HBM_GBPS,
+                           "bytes_per_element": B_HYPERBALL,
+                           "direction": "the stack's dW (the pages do not give MuonH's)"},
+        "adamw": {"elements": n, "ms_per_call": ams, "gbps": agbps,
+                  "frac_hbm_peak": agbps / PEAK_HBM_GBPS, "bytes_per_element": B_ADAMW,
+                  "inputs": "stand-in fp32 vector (the pages do not size the non-matrix "
+                            "parameters)"},
+        "timing": "HIP events around the whole set of calls on the launch stream, eager",
     }
 
 
@@ -437,6 +513,9 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
     }
+    if not args.no_optim:
+        with torch.cuda.stream(side):
+            out["optimizer"] = optimizer_bench(stack, args.steps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(M, args.layers, pow2=args.pow2)
     print(json.dumps(out), flush=True)

@@ -54,6 +54,8 @@ def parse():
     p.add_argument("--pow2", action="store_true",
                    help="power-of-two (E8M0) scales applied by the matrix cores: the library's "
                         "_pow2 variant of every quantiser and GEMM")
+    p.add_argument("--no-overlap", action="store_true",
+                   help="run the timed step in the serial order on one stream")
     p.add_argument("--no-optim", action="store_true",
                    help="skip the optimizer-step measurement")
     p.add_argument("--copy-calibration", action="store_true",
@@ -61,8 +63,31 @@ def parse():
     return p.parse_args()
 
 
+class Op:
+    """One launch of the step: its class, algorithmic flops / bytes, the call bound to the main
+    stream (serial order) and the call bound to its stream in the overlapped order, with the
+    events it waits for before launching and records after."""
+
+    def __init__(self, cls, flops, nbytes, serial, par=None, side=False, waits=(), record=None):
+        self.cls, self.flops, self.bytes = cls, flops, nbytes
+        self.serial, self.par = serial, par or serial
+        self.side, self.waits, self.record = side, tuple(waits), record
+
+
 class Stack:
-    """Device buffers and pre-marshalled launches of the whole step."""
+    """Device buffers and pre-marshalled launches of the whole step.
+
+    Two launch orders over the same kernels and buffers:
+      serial   every launch on one stream, in the step's order (the kernel timing pass);
+      overlap  the critical chain on the main stream and, on a side stream, the work nothing
+               later in the step waits for: each layer's weight quantisation (needed only by
+               that layer's forward GEMMs) runs ahead, and each weight-gradient GEMM (whose dW
+               feeds only the optimizer) runs beside the next linear's gradient quantisation
+               and data-gradient GEMM. Events carry every real dependency: a forward GEMM
+               waits for its layer's weights; a wgrad waits for the quantisation of its dY;
+               a gradient quantisation that reuses a transposed-copy buffer waits for the
+               wgrad that last read it; the step ends when both streams are done.
+    """
 
     def __init__(self, layers: int, M: int, fused: bool = True, pow2: bool = False):
         import torch
@@ -70,15 +95,17 @@ class Stack:
         from blockwise_fp8_gemm_x128_amd import synth
 
         dev = torch.device("cuda:0")
-        self.stream = torch.cuda.current_stream(dev)  # launches are bound to it when prepared
-        self.launches = []  # (kernel class, flops, bytes, callable)
+        self.stream = torch.cuda.current_stream(dev)  # the main stream
+        self.side = torch.cuda.Stream(dev)
         shared = {}
         self.shared = shared  # intermediates reused across layers: keep them allocated
 
         sfx = "_pow2" if pow2 else ""
 
-        def prep(name, *args):
-            return B.prepare(name + sfx, *args)
+        def prep(name, *args, side=False):
+            serial = B.prepare(name + sfx, *args, stream=self.stream)
+            par = B.prepare(name + sfx, *args, stream=self.side) if side else serial
+            return serial, par
 
         def buf(key, shape, dtype):
             if key not in shared:
@@ -87,11 +114,10 @@ class Stack:
 
         self.persist = []
         self.weights = []
-        fwd, bwd = [], []
+        wq_ops, fwd, bwd = [], [], []
         for layer in range(layers):
             group_w, group_q, group_s = [], [], []
-            fwd.append(None)  # the layer's grouped weight quantisation, filled in below
-            wslot = len(fwd) - 1
+            lf = []
             for li, (name, K, N) in enumerate(synth.LINEARS):
                 s = lambda kind: synth.stack_seed(layer, li, kind)  # noqa: E731
                 x = synth.randn_bf16((M, K), synth.X_STD, s(synth.KIND_X), dev)
@@ -106,76 +132,120 @@ class Stack:
                 dyq = buf(("dyq", M, N), (M, N), torch.uint8)
                 sdy = buf(("sdy", M, N), (N // 128, M), torch.float32)
                 dx = buf(("dx", M, K), (M, K), torch.bfloat16)
-                dytq = buf(("dytq", M, N), (N, M), torch.uint8)
-                sdyt = buf(("sdyt", M, N), (M // 128, N), torch.float32)
+                # one transposed-copy buffer per linear slot (shared across layers)
+                dytq = buf(("dytq", li), (N, M), torch.uint8)
+                sdyt = buf(("sdyt", li), (M // 128, N), torch.float32)
                 self.persist += [x, w, dy, wq, sw, dw]
                 self.weights.append((w, dw))  # bf16 copy of the master, and its gradient
                 f = 2.0 * M * N * K
                 group_w.append(w)
                 group_q.append(wq)
                 group_s.append(sw)
-                g_fwd = (f"gemm_fwd{sfx}[{name}]", f, 0.0,
-                         prep("puro_fp8_gemm_fwd", xq, sx, wq, sw, y, M, N, K))
-                g_dgrad = (f"gemm_dgrad{sfx}[{name}]", f, 0.0,
-                           prep("puro_fp8_gemm_dgrad", dyq, sdy, wq, sw, dx, M, N, K))
+                g_fwd = Op(f"gemm_fwd{sfx}[{name}]", f, 0.0,
+                           *prep("puro_fp8_gemm_fwd", xq, sx, wq, sw, y, M, N, K),
+                           waits=(f"wq{layer}",) if li == 0 else ())
+                g_dgrad = Op(f"gemm_dgrad{sfx}[{name}]", f, 0.0,
+                             *prep("puro_fp8_gemm_dgrad", dyq, sdy, wq, sw, dx, M, N, K))
+                # the gradient quantisation that overwrites slot li's transposed copy waits for
+                # the wgrad of the layer above (issued earlier) to have read it
+                reuse = (f"wg{li}",) if layer < layers - 1 else ()
                 if fused:
                     # X's transposed copy lives from this layer's forward to its backward
                     xtq = torch.empty((K, M), dtype=torch.uint8, device=dev)
                     sxt = torch.empty((M // 128, K), dtype=torch.float32, device=dev)
                     self.persist += [xtq, sxt]
-                    fwd += [("quant_dual_1x128" + sfx, 0.0, M * K * B_DUAL,
-                             prep("puro_quant_dual_1x128", x, M, K, xq, sx, xtq, sxt)),
-                            g_fwd]
+                    lf += [Op("quant_dual_1x128" + sfx, 0.0, M * K * B_DUAL,
+                              *prep("puro_quant_dual_1x128", x, M, K, xq, sx, xtq, sxt)),
+                           g_fwd]
                     bwd.append([
-                        ("quant_dual_1x128" + sfx, 0.0, M * N * B_DUAL,
-                         prep("puro_quant_dual_1x128", dy, M, N, dyq, sdy, dytq, sdyt)),
+                        Op("quant_dual_1x128" + sfx, 0.0, M * N * B_DUAL,
+                           *prep("puro_quant_dual_1x128", dy, M, N, dyq, sdy, dytq, sdyt),
+                           waits=reuse, record=f"dual{li}"),
                         g_dgrad,
-                        (f"gemm_wgrad{sfx}[{name}]", f, 0.0,
-                         prep("puro_fp8_gemm_wgrad", dytq, sdyt, xtq, sxt, dw, M, N, K, 0)),
+                        Op(f"gemm_wgrad{sfx}[{name}]", f, 0.0,
+                           *prep("puro_fp8_gemm_wgrad", dytq, sdyt, xtq, sxt, dw, M, N, K, 0,
+                                 side=True),
+                           side=True, waits=(f"dual{li}",), record=f"wg{li}"),
                     ])
                 else:
                     xtq = buf(("xtq", M, K), (K, M), torch.uint8)
                     sxt = buf(("sxt", M, K), (M // 128, K), torch.float32)
-                    fwd += [("quant_act_1x128" + sfx, 0.0, M * K * B_ACT,
-                             prep("puro_quant_act_1x128", x, M, K, xq, sx)),
-                            g_fwd]
+                    lf += [Op("quant_act_1x128" + sfx, 0.0, M * K * B_ACT,
+                              *prep("puro_quant_act_1x128", x, M, K, xq, sx)),
+                           g_fwd]
                     bwd.append([
-                        ("quant_act_1x128" + sfx, 0.0, M * N * B_ACT,
-                         prep("puro_quant_act_1x128", dy, M, N, dyq, sdy)),
+                        Op("quant_act_1x128" + sfx, 0.0, M * N * B_ACT,
+                           *prep("puro_quant_act_1x128", dy, M, N, dyq, sdy)),
                         g_dgrad,
-                        ("quant_transpose" + sfx, 0.0, M * N * B_ACT,
-                         prep("puro_quant_transpose", dy, M, N, dytq, sdyt)),
-                        ("quant_transpose" + sfx, 0.0, M * K * B_ACT,
-                         prep("puro_quant_transpose", x, M, K, xtq, sxt)),
-                        (f"gemm_wgrad{sfx}[{name}]", f, 0.0,
-                         prep("puro_fp8_gemm_wgrad", dytq, sdyt, xtq, sxt, dw, M, N, K, 0)),
+                        # the transposed copies and wgrad only feed dW: all on the side stream,
+                        # whose own order protects the buffers it reuses
+                        Op("quant_transpose" + sfx, 0.0, M * N * B_ACT,
+                           *prep("puro_quant_transpose", dy, M, N, dytq, sdyt, side=True),
+                           side=True),
+                        Op("quant_transpose" + sfx, 0.0, M * K * B_ACT,
+                           *prep("puro_quant_transpose", x, M, K, xtq, sxt, side=True),
+                           side=True),
+                        Op(f"gemm_wgrad{sfx}[{name}]", f, 0.0,
+                           *prep("puro_fp8_gemm_wgrad", dytq, sdyt, xtq, sxt, dw, M, N, K, 0,
+                                 side=True),
+                           side=True),
                     ])
             # all four weights of the layer in one grouped launch
             items = B.w_group_items(group_w, group_q, group_s)
-            fwd[wslot] = ("quant_w_128x128" + sfx, 0.0,
-                          sum(w.shape[0] * w.shape[1] for w in group_w) * B_W,
-                          prep("puro_quant_w_128x128_group", items, len(group_w)))
-        self.launches = fwd + [op for grp in reversed(bwd) for op in grp]
+            wq_op = Op("quant_w_128x128" + sfx, 0.0,
+                       sum(w.shape[0] * w.shape[1] for w in group_w) * B_W,
+                       *prep("puro_quant_w_128x128_group", items, len(group_w), side=True),
+                       side=True, record=f"wq{layer}")
+            wq_ops.append(wq_op)
+            fwd += [wq_op] + lf
+        bwd_flat = [op for grp in reversed(bwd) for op in grp]
+        # serial order: the step as one stream runs it
+        self.launches = fwd + bwd_flat
+        # overlapped issue order: the side stream's weight quantisations first (they record
+        # the events the forward GEMMs wait for), then the forward and backward in step order
+        self.par_order = wq_ops + [op for op in fwd if op not in wq_ops] + bwd_flat
+        self.events = {}
+        for op in self.launches:
+            for e in op.waits + ((op.record,) if op.record else ()):
+                self.events.setdefault(e, torch.cuda.Event())
+        self.fork, self.join = torch.cuda.Event(), torch.cuda.Event()
         self.graph = None
-        self.flops = sum(l[1] for l in self.launches)
-        self.bytes = sum(l[2] for l in self.launches)
+        self.flops = sum(op.flops for op in self.launches)
+        self.bytes = sum(op.bytes for op in self.launches)
 
-    def run(self, events=None):
-        if events is None:
-            for _, _, _, call in self.launches:
-                call()
-        else:
-            for (_, _, _, call), (e0, e1) in zip(self.launches, events):
-                e0.record(self.stream)
-                call()
-                e1.record(self.stream)
+    def run(self, events=None, overlap=False):
+        """One step. `events` (serial only): a (start, end) event pair per launch, recorded
+        around it on the main stream."""
+        if not overlap:
+            if events is None:
+                for op in self.launches:
+                    op.serial()
+            else:
+                for op, (e0, e1) in zip(self.launches, events):
+                    e0.record(self.stream)
+                    op.serial()
+                    e1.record(self.stream)
+            return
+        assert events is None
+        self.fork.record(self.stream)
+        self.side.wait_event(self.fork)
+        for op in self.par_order:
+            st = self.side if op.side else self.stream
+            for e in op.waits:
+                st.wait_event(self.events[e])
+            op.par()
+            if op.record:
+                self.events[op.record].record(st)
+        self.join.record(self.side)
+        self.stream.wait_event(self.join)
 
-    def capture(self):
-        """Capture one whole step (all its launches) as a HIP graph on the stack's stream."""
+    def capture(self, overlap=False):
+        """Capture one whole step (all its launches) as a HIP graph on the main stream (the
+        side stream joins the capture through the fork event)."""
         import torch
         self.graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(self.graph, stream=self.stream):
-            self.run()
+            self.run(overlap=overlap)
 
     def replay(self):
         self.graph.replay()
@@ -376,13 +446,14 @@ def main():
     with torch.cuda.stream(side):  # every launch is bound to this stream when prepared
         stack = Stack(args.layers, M, fused=not args.unfused, pow2=args.pow2)
     torch.cuda.synchronize()
+    overlap = not args.no_overlap
     with torch.cuda.stream(side):
         for _ in range(args.warmup):
-            stack.run()
+            stack.run(overlap=overlap)
     torch.cuda.synchronize()
     use_graph = not args.no_graph
     if use_graph:
-        stack.capture()
+        stack.capture(overlap=overlap)
         stack.replay()  # one untimed replay
         torch.cuda.synchronize()
 
@@ -394,13 +465,15 @@ def main():
             if use_graph:
                 stack.replay()
             else:
-                stack.run()
+                stack.run(overlap=overlap)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
 
-    # Kernel timing pass: the same K steps launched eagerly with a HIP event pair around every
-    # launch on the launch stream (events cannot be placed inside the replayed graph).
+    # Kernel timing pass: the same K steps launched eagerly, in the serial order on the main
+    # stream, with a HIP event pair around every launch (events cannot be placed inside the
+    # replayed graph; the serial order gives each kernel's own duration, not a share of the
+    # chip it had while overlapping another).
     ev_sets = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 for _ in stack.launches] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -414,7 +487,8 @@ def main():
     per_class = {}
     if True:
         for evs in ev_sets:
-            for (cls, fl, by, _), (e0, e1) in zip(stack.launches, evs):
+            for op, (e0, e1) in zip(stack.launches, evs):
+                cls, fl, by = op.cls, op.flops, op.bytes
                 d = per_class.setdefault(cls, {"ms": 0.0, "launches": 0, "flops": 0.0,
                                                "bytes": 0.0})
                 d["ms"] += e0.elapsed_time(e1)
@@ -440,8 +514,8 @@ def main():
         e["ms_per_step"] += v["ms_per_step"]
         e["launches_per_step"] += v["launches_per_step"]
     for kind, e in by_kind.items():
-        fl = sum(l[1] for l in stack.launches if l[0].split("[")[0] == kind)
-        by = sum(l[2] for l in stack.launches if l[0].split("[")[0] == kind)
+        fl = sum(op.flops for op in stack.launches if op.cls.split("[")[0] == kind)
+        by = sum(op.bytes for op in stack.launches if op.cls.split("[")[0] == kind)
         secs = e["ms_per_step"] * 1e-3
         e["avg_launch_us"] = 1e3 * e["ms_per_step"] / e["launches_per_step"]
         if fl:
@@ -472,8 +546,8 @@ def main():
                         "unit": "GB/s", "frac": k["frac_hbm_peak"], **common}
     gemm_ms = sum(v["ms_per_step"] for c, v in kernels.items() if c.startswith("gemm"))
     quant_ms = sum(v["ms_per_step"] for c, v in kernels.items() if c.startswith("quant"))
-    gemm_flops = sum(l[1] for l in stack.launches)
-    quant_bytes = sum(l[2] for l in stack.launches)
+    gemm_flops = sum(op.flops for op in stack.launches)
+    quant_bytes = sum(op.bytes for op in stack.launches)
     roof_ms = (gemm_flops / (PEAK_FP8_TFLOPS * 1e12) + quant_bytes / (PEAK_HBM_GBPS * 1e9)) * 1e3
 
     out = {
@@ -507,7 +581,12 @@ def main():
         "roofline_step_ms": roof_ms,
         "step_frac_of_roofline": roof_ms / ms_per_step,
         "kernel_event_sum_ms_per_step": gemm_ms + quant_ms,
-        "timed_region": "one captured HIP graph replay per step" if use_graph else "eager launches",
+        "timed_region": ("one captured HIP graph replay per step" if use_graph
+                         else "eager launches"),
+        "launch_order": ("overlapped: critical chain on the main stream; weight quantisation "
+                         "and weight-gradient GEMMs on a side stream, joined by events"
+                         if overlap else "serial, one stream"),
+        "kernel_timing": "HIP event pair per launch, serial order on one stream",
         "kernel_timing_pass_ms_per_step": eager_ms_per_step,
         "kernels_by_kind": by_kind,
         "kernels": kernels,

@@ -254,10 +254,11 @@ puro_fp8_gemm_dgrad_pow2 = _pow2_variant(puro_fp8_gemm_dgrad)
 puro_fp8_gemm_wgrad_pow2 = _pow2_variant(puro_fp8_gemm_wgrad)
 
 
-def prepare(name: str, *args):
+def prepare(name: str, *args, stream=None):
     """Pre-marshalled call of a C entry point for hot loops: tensors become raw device
-    pointers, the current torch stream is bound, and the returned zero-argument callable
-    only crosses into the C ABI (which still validates) and checks the status."""
+    pointers, `stream` (a torch.cuda.Stream; default the current torch stream) is bound, and the
+    returned zero-argument callable only crosses into the C ABI (which still validates) and
+    checks the status."""
     fn = getattr(lib(), name)
     dev = None
     conv = []
@@ -267,8 +268,7 @@ def prepare(name: str, *args):
             conv.append(a.data_ptr())
         else:
             conv.append(a)
-    stream = _stream(dev)
-    conv.append(stream)
+    conv.append(stream.cuda_stream if stream is not None else _stream(dev))
 
     keep = tuple(args)  # tensors and ctypes arrays the raw arguments point into
 

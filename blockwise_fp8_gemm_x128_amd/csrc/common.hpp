@@ -39,11 +39,14 @@ inline puro_status launch_status() {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// fp32 -> bf16 bits, round to nearest even (inputs are finite).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two fp32 -> two bf16 packed in one dword (lo in bits 0-15), round to nearest even: gfx950
+// converts both in one v_cvt_pk_bf16_f32 (checked on MI355X against the integer
+// round-to-nearest-even rule, denormals included).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // Four fp32 values, already multiplied by the group's reciprocal scale, to four OCP E4M3 bytes

@@ -535,8 +535,8 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A,
         *out = accumulate ? *out + v : v;
       } else {
         v2i packed;
-        packed[0] = static_cast<int>(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16));
-        packed[1] = static_cast<int>(f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16));
+        packed[0] = static_cast<int>(pack_bf16x2(v[0], v[1]));
+        packed[1] = static_cast<int>(pack_bf16x2(v[2], v[3]));
         *reinterpret_cast<v2i*>(static_cast<uint16_t*>(Cout) + row * J + col) = packed;
       }
     }

@@ -94,8 +94,8 @@ __global__ __launch_bounds__(kOptThreads) void finish_kernel(const double* __res
 
 __device__ __forceinline__ uint2 bf16x4(float4 a) {
   uint2 o;
-  o.x = f32_to_bf16_rne(a.x) | (f32_to_bf16_rne(a.y) << 16);
-  o.y = f32_to_bf16_rne(a.z) | (f32_to_bf16_rne(a.w) << 16);
+  o.x = pack_bf16x2(a.x, a.y);
+  o.y = pack_bf16x2(a.z, a.w);
   return o;
 }
 

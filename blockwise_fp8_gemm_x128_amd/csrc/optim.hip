@@ -9,8 +9,8 @@
 // bf16 copy the next step's 128x128 weight quantiser reads.
 //
 // All of it is HBM-bound streaming: 16 B per lane per access, grid-stride loops, and a
-// deterministic two-level reduction (fp64 per lane and per block, then one block summing the
-// block partials in index order) whose grid depends on the element count only, so results are
+// deterministic two-level reduction (fp64 per lane and per block, then the block partials
+// summed in one fixed order) whose grid depends on the element count only, so results are
 // reproducible run to run and device to device.
 #include <math.h>
 
@@ -21,9 +21,8 @@ namespace {
 
 constexpr int kOptThreads = 256;
 constexpr int kOptMaxBlocks = PURO_OPT_MAX_BLOCKS;
-// workspace layout: [kOptMaxBlocks] double partial sums, then the scale factor (float)
-constexpr size_t kFactorOff = sizeof(double) * kOptMaxBlocks;
-static_assert(kFactorOff + 16 <= PURO_OPT_WORKSPACE_BYTES, "workspace too small");
+// workspace layout: [kOptMaxBlocks] double partial sums
+static_assert(sizeof(double) * kOptMaxBlocks <= PURO_OPT_WORKSPACE_BYTES, "workspace too small");
 
 // Blocks of a reduction over n4 16-byte vectors: about four vectors per lane, at most
 // kOptMaxBlocks.
@@ -74,22 +73,21 @@ __global__ __launch_bounds__(kOptThreads) void sumsq_kernel(const float* src,
   if (threadIdx.x == 0) partials[blockIdx.x] = s;
 }
 
-// One block: total of the partials in a fixed order, the norm, and the projection factor
-// radius / norm (1 for a zero matrix, which has no direction to scale).
-__global__ __launch_bounds__(kOptThreads) void finish_kernel(const double* __restrict__ partials,
-                                                             int count,
-                                                             const float* __restrict__ radius,
-                                                             float* __restrict__ factor,
-                                                             float* __restrict__ norm) {
-  __shared__ double sh[kOptThreads / 64];
+// Total of the block partials, summed in the same fixed order by whichever block asks (so every
+// block of a launch gets the same value bit for bit).
+__device__ __forceinline__ double total_of(const double* __restrict__ partials, int count,
+                                          double* sh) {
   double acc = 0.0;
   for (int i = threadIdx.x; i < count; i += kOptThreads) acc += partials[i];
-  const double ss = block_sum(acc, sh);
-  if (threadIdx.x == 0) {
-    const double nrm = sqrt(ss);
-    if (norm) *norm = static_cast<float>(nrm);
-    if (factor) *factor = ss > 0.0 ? static_cast<float>(double(*radius) / nrm) : 1.0f;
-  }
+  return block_sum(acc, sh);
+}
+
+// One block: the norm.
+__global__ __launch_bounds__(kOptThreads) void norm_kernel(const double* __restrict__ partials,
+                                                           int count, float* __restrict__ norm) {
+  __shared__ double sh[kOptThreads / 64];
+  const double ss = total_of(partials, count, sh);
+  if (threadIdx.x == 0) *norm = static_cast<float>(sqrt(ss));
 }
 
 __device__ __forceinline__ uint2 bf16x4(float4 a) {
@@ -99,11 +97,17 @@ __device__ __forceinline__ uint2 bf16x4(float4 a) {
   return o;
 }
 
-// w <- w * factor, and its bf16 copy.
+// w <- w * factor, and its bf16 copy. Every block first forms the factor radius / ||v|| itself
+// from the partials (1 for a zero matrix, which has no direction to scale): 16 KB of cached
+// reads per block instead of a dependent single-block launch.
 __global__ __launch_bounds__(kOptThreads) void scale_kernel(float* __restrict__ w, int64_t n4,
-                                                            const float* __restrict__ factor,
+                                                            const double* __restrict__ partials,
+                                                            int count,
+                                                            const float* __restrict__ radius,
                                                             uint16_t* __restrict__ wbf) {
-  const float f = *factor;
+  __shared__ double sh[kOptThreads / 64];
+  const double ss = total_of(partials, count, sh);
+  const float f = ss > 0.0 ? static_cast<float>(double(*radius) / sqrt(ss)) : 1.0f;
   float4* w4 = reinterpret_cast<float4*>(w);
   uint2* b4 = reinterpret_cast<uint2*>(wbf);
   for (int64_t i = int64_t(blockIdx.x) * kOptThreads + threadIdx.x; i < n4;
@@ -184,8 +188,7 @@ extern "C" puro_status puro_frobenius_norm(const float* w, int64_t numel, float*
   double* partials = static_cast<double*>(workspace);
   hipLaunchKernelGGL(sumsq_kernel<false>, dim3(blocks), dim3(kOptThreads), 0, s, w, nullptr,
                      nullptr, n4, 0.0f, partials);
-  hipLaunchKernelGGL(finish_kernel, dim3(1), dim3(kOptThreads), 0, s, partials, blocks,
-                     nullptr, nullptr, norm);
+  hipLaunchKernelGGL(norm_kernel, dim3(1), dim3(kOptThreads), 0, s, partials, blocks, norm);
   return launch_status();
 }
 
@@ -205,13 +208,11 @@ extern "C" puro_status puro_hyperball_step(float* w, const float* u, int64_t num
   const int64_t n4 = numel / 4;
   const int blocks = opt_blocks(n4);
   double* partials = static_cast<double*>(workspace);
-  float* factor = reinterpret_cast<float*>(static_cast<char*>(workspace) + kFactorOff);
   hipLaunchKernelGGL(sumsq_kernel<true>, dim3(blocks), dim3(kOptThreads), 0, s, w, u, w, n4, lr,
                      partials);
-  hipLaunchKernelGGL(finish_kernel, dim3(1), dim3(kOptThreads), 0, s, partials, blocks, radius,
-                     factor, nullptr);
-  hipLaunchKernelGGL(scale_kernel, dim3(stream_blocks(n4)), dim3(kOptThreads), 0, s, w, n4,
-                     factor, static_cast<uint16_t*>(w_bf16));
+  // the same grid as the reduction: each block re-sums the partials, so keep it small
+  hipLaunchKernelGGL(scale_kernel, dim3(blocks), dim3(kOptThreads), 0, s, w, n4, partials, blocks,
+                     radius, static_cast<uint16_t*>(w_bf16));
   return launch_status();
 }
 

@@ -218,16 +218,17 @@ __global__ __launch_bounds__(256) void quant_transpose_kernel(const uint16_t* __
 }
 
 // ------------------------------------------------------------------ both orientations at once
-// One block per 128x128 tile of x, read from HBM once. Pass 1: 16 lanes per 256 B row, 8 passes
-// of 16 rows; each row's 128 values form one row group (quantised and stored from registers)
-// and are also staged in LDS as dwords with a 65-dword row pitch. Pass 2: as in the transposed
-// quantiser, 8 lanes per column pair, each holding 16 rows, so a column's amax is an 8-lane
-// reduction and its 128 output bytes are one contiguous 128 B segment; 64 column pairs, two
-// rounds of 32.
+// One 512-thread block per 128x128 tile of x, read from HBM once. Pass 1: 16 lanes per 256 B
+// row, 4 passes of 32 rows; each row's 128 values form one row group (quantised and stored from
+// registers) and are also staged in LDS as dwords with a 65-dword row pitch. Pass 2: as in the
+// transposed quantiser, 8 lanes per column pair, each holding 16 rows, so a column's amax is an
+// 8-lane reduction and its 128 output bytes are one contiguous 128 B segment; the 8 waves cover
+// the 64 column pairs in one round. (Eight waves per block rather than four: twice the waves
+// per CU for the same 33 KB of LDS, measured 2 % faster over the model's shapes.)
 constexpr int kDualPitch = 65;  // dwords per staged row (64 data + 1 pad)
 
 template <bool kPow2>
-__global__ __launch_bounds__(256) void quant_dual_1x128_kernel(
+__global__ __launch_bounds__(512) void quant_dual_1x128_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, uint8_t* __restrict__ q,
     float* __restrict__ s, uint8_t* __restrict__ qt, float* __restrict__ st) {
   __shared__ uint32_t tile[128 * kDualPitch];
@@ -239,13 +240,13 @@ __global__ __launch_bounds__(256) void quant_dual_1x128_kernel(
 
   {
     const int seg = t >> 4, l16 = t & 15;
-    uint4 v[8];
+    uint4 v[4];
 #pragma unroll
-    for (int p = 0; p < 8; ++p)
-      v[p] = *reinterpret_cast<const uint4*>(x + (m0 + 16 * p + seg) * cols + c0 + l16 * 8);
+    for (int p = 0; p < 4; ++p)
+      v[p] = *reinterpret_cast<const uint4*>(x + (m0 + 32 * p + seg) * cols + c0 + l16 * 8);
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int r = 16 * p + seg;
+    for (int p = 0; p < 4; ++p) {
+      const int r = 32 * p + seg;
       uint32_t* dst = tile + r * kDualPitch + l16 * 4;
       dst[0] = v[p].x;
       dst[1] = v[p].y;
@@ -271,9 +272,8 @@ __global__ __launch_bounds__(256) void quant_dual_1x128_kernel(
 
   const int lane = t & 63, w = t >> 6;
   const int pair = lane & 7, g = lane >> 3;
-#pragma unroll
-  for (int round = 0; round < 2; ++round) {
-    const int dc = round * 32 + w * 8 + pair;  // dword column: tile columns 2*dc, 2*dc+1
+  {
+    const int dc = w * 8 + pair;  // dword column: tile columns 2*dc, 2*dc+1
     uint32_t d[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) d[i] = tile[(16 * g + i) * kDualPitch + dc];
@@ -292,22 +292,14 @@ __global__ __launch_bounds__(256) void quant_dual_1x128_kernel(
     scale_rule<kPow2>(m0v, s0, r0);
     scale_rule<kPow2>(m1v, s1, r1);
     uint4 o0, o1;
-    o0.x = e4m3x4(bf16_lo(d[0]) * r0, bf16_lo(d[1]) * r0, bf16_lo(d[2]) * r0,
-                  bf16_lo(d[3]) * r0);
-    o0.y = e4m3x4(bf16_lo(d[4]) * r0, bf16_lo(d[5]) * r0, bf16_lo(d[6]) * r0,
-                  bf16_lo(d[7]) * r0);
-    o0.z = e4m3x4(bf16_lo(d[8]) * r0, bf16_lo(d[9]) * r0, bf16_lo(d[10]) * r0,
-                  bf16_lo(d[11]) * r0);
-    o0.w = e4m3x4(bf16_lo(d[12]) * r0, bf16_lo(d[13]) * r0, bf16_lo(d[14]) * r0,
-                  bf16_lo(d[15]) * r0);
-    o1.x = e4m3x4(bf16_hi(d[0]) * r1, bf16_hi(d[1]) * r1, bf16_hi(d[2]) * r1,
-                  bf16_hi(d[3]) * r1);
-    o1.y = e4m3x4(bf16_hi(d[4]) * r1, bf16_hi(d[5]) * r1, bf16_hi(d[6]) * r1,
-                  bf16_hi(d[7]) * r1);
-    o1.z = e4m3x4(bf16_hi(d[8]) * r1, bf16_hi(d[9]) * r1, bf16_hi(d[10]) * r1,
-                  bf16_hi(d[11]) * r1);
-    o1.w = e4m3x4(bf16_hi(d[12]) * r1, bf16_hi(d[13]) * r1, bf16_hi(d[14]) * r1,
-                  bf16_hi(d[15]) * r1);
+    o0.x = e4m3x4(bf16_lo(d[0]) * r0, bf16_lo(d[1]) * r0, bf16_lo(d[2]) * r0, bf16_lo(d[3]) * r0);
+    o0.y = e4m3x4(bf16_lo(d[4]) * r0, bf16_lo(d[5]) * r0, bf16_lo(d[6]) * r0, bf16_lo(d[7]) * r0);
+    o0.z = e4m3x4(bf16_lo(d[8]) * r0, bf16_lo(d[9]) * r0, bf16_lo(d[10]) * r0, bf16_lo(d[11]) * r0);
+    o0.w = e4m3x4(bf16_lo(d[12]) * r0, bf16_lo(d[13]) * r0, bf16_lo(d[14]) * r0, bf16_lo(d[15]) * r0);
+    o1.x = e4m3x4(bf16_hi(d[0]) * r1, bf16_hi(d[1]) * r1, bf16_hi(d[2]) * r1, bf16_hi(d[3]) * r1);
+    o1.y = e4m3x4(bf16_hi(d[4]) * r1, bf16_hi(d[5]) * r1, bf16_hi(d[6]) * r1, bf16_hi(d[7]) * r1);
+    o1.z = e4m3x4(bf16_hi(d[8]) * r1, bf16_hi(d[9]) * r1, bf16_hi(d[10]) * r1, bf16_hi(d[11]) * r1);
+    o1.w = e4m3x4(bf16_hi(d[12]) * r1, bf16_hi(d[13]) * r1, bf16_hi(d[14]) * r1, bf16_hi(d[15]) * r1);
     const int64_t col = c0 + 2 * dc;
     *reinterpret_cast<uint4*>(qt + col * rows + m0 + 16 * g) = o0;
     *reinterpret_cast<uint4*>(qt + (col + 1) * rows + m0 + 16 * g) = o1;
@@ -384,7 +376,7 @@ puro_status quant_dual_1x128(const void* x, int64_t rows, int64_t cols, void* q,
   const int64_t blocks = (rows / 128) * (cols / 128);
   if (blocks > INT32_MAX) return PURO_ERR_SHAPE;
   hipLaunchKernelGGL(quant_dual_1x128_kernel<kPow2>, dim3(static_cast<uint32_t>(blocks)),
-                     dim3(256), 0, static_cast<hipStream_t>(stream),
+                     dim3(512), 0, static_cast<hipStream_t>(stream),
                      static_cast<const uint16_t*>(x), rows, cols, static_cast<uint8_t*>(q), s,
                      static_cast<uint8_t*>(qt), st);
   return launch_status();

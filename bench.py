@@ -434,7 +434,7 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(multi-GPU runs are out of scope: the path shards by data parallelism, see the "
               "design notes)", file=sys.stderr)
         sys.exit(2)

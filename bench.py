@@ -54,8 +54,12 @@ def parse():
     p.add_argument("--pow2", action="store_true",
                    help="power-of-two (E8M0) scales applied by the matrix cores: the library's "
                         "_pow2 variant of every quantiser and GEMM")
-    p.add_argument("--no-overlap", action="store_true",
-                   help="run the timed step in the serial order on one stream")
+    order = p.add_mutually_exclusive_group()
+    order.add_argument("--overlap", action="store_true",
+                       help="time the step in the two-stream order (weight quantisation and wgrad "
+                            "on a side stream; measured no faster than the serial order on MI355X)")
+    order.add_argument("--no-overlap", action="store_true",
+                       help="time the step in the serial order on one stream (the default)")
     p.add_argument("--no-optim", action="store_true",
                    help="skip the optimizer-step measurement")
     p.add_argument("--copy-calibration", action="store_true",
@@ -446,7 +450,7 @@ def main():
     with torch.cuda.stream(side):  # every launch is bound to this stream when prepared
         stack = Stack(args.layers, M, fused=not args.unfused, pow2=args.pow2)
     torch.cuda.synchronize()
-    overlap = not args.no_overlap
+    overlap = args.overlap
     with torch.cuda.stream(side):
         for _ in range(args.warmup):
             stack.run(overlap=overlap)

@@ -6,6 +6,8 @@
 // Every scale is constant over one 128-long reduction chunk, so each chunk's dot products are
 // taken on the matrix cores (exact FP8 products, fp32 sums) and then promoted into an fp32
 // accumulator:   acc += (s_a * s_b) * P_chunk.
+// The power-of-two variant (a library option: scales 2^e) hands each operand row's exponent
+// to the scaled FP8 instruction instead, which applies it and accumulates every chunk itself.
 //
 // All three GEMMs are one kernel template computing
 //     C[i][j] = sum_c sA[c][i] * sB(c, j) * sum_{l in chunk c} A[i][l] * B(j, l)

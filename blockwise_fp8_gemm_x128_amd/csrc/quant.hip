@@ -1,14 +1,16 @@
-// Blockwise FP8 quantisers for gfx950: 1x128 row groups, 128x128 weight blocks, and the
-// transposed 1x128 requantisation used by the weight-gradient GEMM.
+// Blockwise FP8 quantisers for gfx950: 1x128 row groups, 128x128 weight blocks (one matrix or
+// several in one launch), the transposed 1x128 requantisation used by the weight-gradient GEMM,
+// and both 1x128 orientations from one read.
 //
 // Method: Paper walkthrough: Puro-2B (ta-paperlens.web.app), section "Lever 2: use blockwise
 // FP8 from step zero" — scales are taken per local group, activations and their gradients in
 // groups of 128 along the reduction dimension and weights in 128x128 blocks. Number formats
-// and rounding as stated in include/puro.h.
+// and rounding as stated in include/puro.h. Every kernel is instantiated for two scale rules:
+// amax/448 (the reading of the pages) and the power of two at or above it (a library option).
 //
-// All three kernels are HBM-bound: each bf16 element is read once (2 B) and its E4M3 code
-// written once (1 B), plus one fp32 scale per group. Loads are 16 B per lane and every wave
-// instruction touches whole 128 B (or larger) segments; all per-element arithmetic (widen,
+// All of them are HBM-bound: each bf16 element is read once (2 B) and each of its E4M3 codes
+// written once (1 B per copy), plus one fp32 scale per group. Loads are 16 B per lane and every
+// wave instruction touches whole 128 B (or larger) segments; all per-element arithmetic (widen,
 // |max|, multiply, clamp, packed convert) stays in registers.
 #include "common.hpp"
 

@@ -23,11 +23,11 @@
 // c+1 (A tile, B tile and the A/B scale rows) streams into the other stage with
 // buffer_load_dwordx4 ... lds, which writes LDS directly (no VGPR staging, no ds_write). One
 // barrier per chunk separates "stage landed" from "stage free". Each 128-byte row of a staged
-// operand keeps its eight 16-byte pieces XOR-permuted (piece p at slot p ^ swz(row)). gfx950
-// serves a 16-byte-per-lane LDS read 32 lanes at a time over a 512-byte bank window, and an
-// 8-byte transposed read 64 lanes at a time; the two swizzles below make the MFMA fragment
-// reads (16 rows x 2 lane groups per pass) and the transposed reads (4 lane groups x 8 rows x
-// 2 halves) hit distinct bank slots.
+// operand keeps its eight 16-byte pieces XOR-permuted (piece p at slot p ^ swz(row)). The two
+// swizzles below were chosen by measurement on MI355X (SQ_LDS_BANK_CONFLICT of each candidate's
+// exact read pattern): both the 16-byte fragment reads (16 rows x 4 lane groups) and the 8-byte
+// transposed reads (4 lane groups x 8 rows x 2 halves) run with no bank-conflict cycles, where
+// the unswizzled layout costs 12 and 14 cycles per read instruction.
 //
 // Block order: workgroups are dispatched round-robin over the 8 XCDs, so the block id is first
 // remapped so that consecutive tiles run on one XCD (sharing that XCD's L2), and tiles are
@@ -89,12 +89,13 @@ struct Cfg {
   static_assert(!kBTrans || WN == 64, "reduction-major B fragment offsets assume WN = 64");
 };
 
-// Swizzle of row-major staged operands (A, and B of forward / wgrad): row bits 2 and 3 -> slot
-// bits 0 and 2 (bit 1 is left to the lane group of the fragment read).
-__device__ __forceinline__ int swz_rows(int row) { return ((row >> 2) & 1) | ((row >> 1) & 4); }
-// Swizzle of reduction-major slabs (B of dgrad): row bit 2 -> slot bit 0, row bits 5-6 -> slot
-// bits 1-2.
-__device__ __forceinline__ int swz_slab(int row) { return ((row >> 2) & 1) | ((row >> 4) & 6); }
+// Swizzle of row-major staged operands (A, and B of forward / wgrad): row bits 0-1 -> slot bits
+// 1-2, row bit 3 -> slot bit 0. It depends on row bits 0-3 only, as the loader and the fragment
+// offsets below require.
+__device__ __forceinline__ int swz_rows(int row) { return ((row & 3) << 1) | ((row >> 3) & 1); }
+// Swizzle of reduction-major slabs (B of dgrad): row bits 1-2 -> slot bits 0-1, row bit 5 ->
+// slot bit 2. It ignores row bits 3-4, as the transposed fragment offsets below require.
+__device__ __forceinline__ int swz_slab(int row) { return ((row >> 1) & 3) | ((row >> 3) & 4); }
 
 __device__ __forceinline__ int64_t imin64(int64_t a, int64_t b) { return a < b ? a : b; }
 
@@ -222,7 +223,8 @@ struct Loader {
 // Per-lane LDS byte offsets of this wave's fragment reads, fixed for the whole kernel. Every
 // row-major fragment covers 16 staged rows starting at a multiple of 16, so its swizzle term
 // swz_rows(R0 + r) = swz_rows(r) depends on the lane only; every transposed read of lane
-// 16G + r touches slab row 32G + 8i + r/2, whose swz_slab term is (r >> 3) | 2G for all i.
+// 16G + r touches slab row 32G + 8i + r/2, whose swz_slab term is the same for all i (row bits
+// 3-4 do not enter it).
 template <class C>
 struct FragOffsets {
   int a[2];    // [half]: A rows, wave-relative

@@ -33,6 +33,11 @@
 // remapped so that consecutive tiles run on one XCD (sharing that XCD's L2), and tiles are
 // walked in bands of 8 tile-rows, column by column, so concurrently running tiles share A and B
 // panels.
+//
+// Split reduction: a weight gradient whose 128x128 tiles would leave the four-wave blocks one
+// wave per SIMD (at most one tile per CU) runs two groups of four waves per tile instead, group
+// g multiplying out chunks g, g+2, g+4, ... from stages of its own; group 1 then hands its
+// partial sums to group 0 through LDS, which adds them in a fixed order and stores the tile.
 #include <type_traits>
 
 #include "common.hpp"
@@ -448,13 +453,11 @@ __device__ __forceinline__ void compute_chunk_pow2(const lds_u8* stage, float sb
     for (int nj = 0; nj < C::NJ; ++nj) asm volatile("" : "+v"(acc[mi][nj]));
 }
 
+// Tile origin of this block. Workgroups are dealt round-robin to the 8 XCDs, so the block id is
+// first remapped so that consecutive tiles run on one XCD; tiles are then walked in bands of
+// kGroupRows tile-rows, column by column.
 template <class C>
-__device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A,
-                                          const float* __restrict__ sA,
-                                          const uint8_t* __restrict__ B,
-                                          const float* __restrict__ sB, void* __restrict__ Cout,
-                                          int64_t I, int64_t J, int64_t L, int accumulate,
-                                          lds_u8* stage0, lds_u8* stage1) {
+__device__ __forceinline__ void tile_origin(int64_t I, int64_t J, int64_t& i0, int64_t& j0) {
   const int64_t tiles_i = (I + C::BM - 1) / C::BM;
   const int64_t tiles_j = (J + C::BN - 1) / C::BN;
   const int64_t nwg = tiles_i * tiles_j;
@@ -465,7 +468,48 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A,
   const int64_t local = b - band * kGroupRows * tiles_j;
   const int64_t ti = band * kGroupRows + local % band_rows;
   const int64_t tj = local / band_rows;
-  const int64_t i0 = uniform64(ti * C::BM), j0 = uniform64(tj * C::BN);
+  i0 = uniform64(ti * C::BM);
+  j0 = uniform64(tj * C::BN);
+}
+
+// Epilogue: lane (G, r) holds row r, columns 4G..4G+3 of every 16x16 block: one 8-byte (bf16)
+// or 16-byte (fp32) store per block.
+template <class C>
+__device__ __forceinline__ void store_tile(const v4f (&acc)[C::MI][C::NJ], void* Cout, int64_t I,
+                                           int64_t J, int64_t i0, int64_t j0, int wm, int wn,
+                                           int lane, int accumulate) {
+  const int G = lane >> 4, r16 = lane & 15;
+  const int64_t r0 = i0 + wm * C::WM, q0 = j0 + wn * C::WN;
+  if (r0 >= I || q0 >= J) return;  // this wave lies in the invalid half of an edge tile
+#pragma unroll
+  for (int mi = 0; mi < C::MI; ++mi) {
+#pragma unroll
+    for (int nj = 0; nj < C::NJ; ++nj) {
+      const int64_t row = r0 + 16 * mi + r16;
+      const int64_t col = q0 + 16 * nj + 4 * G;
+      const v4f v = acc[mi][nj];
+      if (C::kOutF32) {
+        v4f* out = reinterpret_cast<v4f*>(static_cast<float*>(Cout) + row * J + col);
+        *out = accumulate ? *out + v : v;
+      } else {
+        v2i packed;
+        packed[0] = static_cast<int>(pack_bf16x2(v[0], v[1]));
+        packed[1] = static_cast<int>(pack_bf16x2(v[2], v[3]));
+        *reinterpret_cast<v2i*>(static_cast<uint16_t*>(Cout) + row * J + col) = packed;
+      }
+    }
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A,
+                                          const float* __restrict__ sA,
+                                          const uint8_t* __restrict__ B,
+                                          const float* __restrict__ sB, void* __restrict__ Cout,
+                                          int64_t I, int64_t J, int64_t L, int accumulate,
+                                          lds_u8* stage0, lds_u8* stage1) {
+  int64_t i0, j0;
+  tile_origin<C>(I, J, i0, j0);
 
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -522,28 +566,102 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A,
   }
   if (c < nk) half(stage0, stage1, c);
 
-  // Epilogue: lane (G, r) holds row r, columns 4G..4G+3 of every 16x16 block: one 8-byte (bf16)
-  // or 16-byte (fp32) store per block.
-  const int G = lane >> 4, r16 = lane & 15;
-  const int64_t r0 = i0 + wm * C::WM, q0 = j0 + wn * C::WN;
-  if (r0 >= I || q0 >= J) return;  // this wave lies in the invalid half of an edge tile
+  store_tile<C>(acc, Cout, I, J, i0, j0, wm, wn, lane, accumulate);
+}
+
+// Weight gradient of a small output with the reduction split inside the block: two groups of
+// the configuration's waves share one BM x BN tile, group g multiplying out chunks g, g+2, g+4,
+// ... from stages of its own, so a 128 x 128 tile gets 8 waves (two per SIMD) instead of 4.
+// At the end group 1 hands its partial sums to group 0 through LDS, which adds them (fixed
+// order, so the result is deterministic) and stores the tile.
+constexpr int kRedPitch = 132;  // floats per row of the reduction buffer
+
+template <class C>
+__device__ __forceinline__ void gemm_body_k2(const uint8_t* __restrict__ A,
+                                             const float* __restrict__ sA,
+                                             const uint8_t* __restrict__ B,
+                                             const float* __restrict__ sB, void* __restrict__ Cout,
+                                             int64_t I, int64_t J, int64_t L, int accumulate,
+                                             lds_u8* stage0, lds_u8* stage1) {
+  static_assert(C::mode == kWgrad, "split reduction is a weight-gradient shape");
+  static_assert(C::BM * kRedPitch * 4 <= 2 * C::kStageBytes, "reduction buffer fits a stage pair");
+  int64_t i0, j0;
+  tile_origin<C>(I, J, i0, j0);
+  const int t = threadIdx.x;
+  const int wave_all = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int g = wave_all / C::kWaves;  // reduction group
+  const int wave = wave_all % C::kWaves;
+  const int lane = t & 63;
+  const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
+  const int64_t nk = L / kChunk;
+
+  Loader<C> ld;
+  ld.A = A;
+  ld.B = B;
+  ld.sA = sA;
+  ld.sB = sB;
+  ld.I = I;
+  ld.J = J;
+  ld.L = L;
+  ld.i0 = i0;
+  ld.j0 = j0;
+  ld.wave = wave;
+  ld.lane = lane;
+  ld.init(wn);
+  FragOffsets<C> fo;
+  fo.init(wm, wn, lane);
+
+  v4f acc[C::MI][C::NJ];
 #pragma unroll
-  for (int mi = 0; mi < C::MI; ++mi) {
+  for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
-    for (int nj = 0; nj < C::NJ; ++nj) {
-      const int64_t row = r0 + 16 * mi + r16;
-      const int64_t col = q0 + 16 * nj + 4 * G;
-      const v4f v = acc[mi][nj];
-      if (C::kOutF32) {
-        v4f* out = reinterpret_cast<v4f*>(static_cast<float*>(Cout) + row * J + col);
-        *out = accumulate ? *out + v : v;
-      } else {
-        v2i packed;
-        packed[0] = static_cast<int>(pack_bf16x2(v[0], v[1]));
-        packed[1] = static_cast<int>(pack_bf16x2(v[2], v[3]));
-        *reinterpret_cast<v2i*>(static_cast<uint16_t*>(Cout) + row * J + col) = packed;
-      }
+    for (int nj = 0; nj < C::NJ; ++nj) acc[mi][nj] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // group g's stages: [g * kStageBytes, (g + 1) * kStageBytes) of each stage object
+  const int goff = g * C::kStageBytes;
+  if (g < nk) ld.issue(stage0 + goff, g);
+  auto half = [&](lds_u8* cur, lds_u8* nxt, int64_t p) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int64_t cn = 2 * (p + 1) + g;
+    if (cn < nk) ld.issue(nxt + goff, cn);
+    if (2 * p + g < nk) {
+      if constexpr (C::kPow2)
+        compute_chunk_pow2<C>(cur + goff, 0.0f, fo, acc);
+      else
+        compute_chunk<C>(cur + goff, 0.0f, fo, acc);
     }
+  };
+  const int64_t steps = (nk + 1) / 2;
+  int64_t p = 0;
+  for (; p + 1 < steps; p += 2) {
+    half(stage0, stage1, p);
+    half(stage1, stage0, p + 1);
+  }
+  if (p < steps) half(stage0, stage1, p);
+
+  // reduction through LDS (both stage objects are free once every wave has passed this barrier)
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const int G = lane >> 4, r16 = lane & 15;
+  lds_f32* red = reinterpret_cast<lds_f32*>(stage0);
+  if (g == 1) {
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+      for (int nj = 0; nj < C::NJ; ++nj)
+        *reinterpret_cast<lds_v4f*>(red + (wm * C::WM + 16 * mi + r16) * kRedPitch +
+                                    wn * C::WN + 16 * nj + 4 * G) = acc[mi][nj];
+  }
+  __syncthreads();
+  if (g == 0) {
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+      for (int nj = 0; nj < C::NJ; ++nj)
+        acc[mi][nj] += *reinterpret_cast<const lds_v4f*>(
+            red + (wm * C::WM + 16 * mi + r16) * kRedPitch + wn * C::WN + 16 * nj + 4 * G);
+    store_tile<C>(acc, Cout, I, J, i0, j0, wm, wn, lane, accumulate);
   }
 }
 
@@ -600,6 +718,20 @@ PURO_GEMM_KERNEL(gemm_wgrad_128x128_pow2, WgradSmallP2)
 PURO_GEMM_KERNEL(gemm_wgrad_256x192_pow2, WgradWideP2)
 PURO_GEMM_KERNEL(gemm_wgrad_192x256_pow2, WgradTallP2)
 
+#define PURO_GEMM_KERNEL_K2(NAME, CFG)                                                     \
+  __global__ __launch_bounds__(2 * CFG::kThreads) void NAME(                               \
+      const uint8_t* __restrict__ A, const float* __restrict__ sA,                         \
+      const uint8_t* __restrict__ B, const float* __restrict__ sB, void* __restrict__ Cout, \
+      int64_t I, int64_t J, int64_t L, int accumulate) {                                   \
+    __shared__ __attribute__((aligned(1024))) uint8_t stage0[2 * CFG::kStageBytes];        \
+    __shared__ __attribute__((aligned(1024))) uint8_t stage1[2 * CFG::kStageBytes];        \
+    gemm_body_k2<CFG>(A, sA, B, sB, Cout, I, J, L, accumulate, (lds_u8*)stage0,            \
+                      (lds_u8*)stage1);                                                     \
+  }
+
+PURO_GEMM_KERNEL_K2(gemm_wgrad_128x128_k2, WgradSmall)
+PURO_GEMM_KERNEL_K2(gemm_wgrad_128x128_k2_pow2, WgradSmallP2)
+
 // Number of compute units the big tiles must at least fill once.
 constexpr int64_t kComputeUnits = 256;
 
@@ -619,10 +751,14 @@ inline int64_t device_cus() {
 
 // Weight-gradient tile shape: the candidate with the least estimated time, counting whole
 // rounds of tiles over the chip (a partial last round costs a full one), each tile's area,
-// the blocks resident per CU (LDS and registers allow one 8-wave block of the 256-row shapes
-// or two 4-wave 128x128 blocks), and a per-shape efficiency measured on MI355X (bigger tiles
-// re-read less). The 192- and 256-wide shapes are only used when they tile the output exactly.
-enum WgradShape { kW256x256, kW128x128, kW256x192, kW192x256 };
+// the blocks resident per CU (LDS and registers allow one 8-wave block of the 256-row shapes,
+// two 4-wave 128x128 blocks, or one 8-wave split-reduction 128x128 block), and a per-shape
+// efficiency measured on MI355X (bigger tiles re-read less). The 192- and 256-wide shapes are
+// only used when they tile the output exactly. The split-reduction figure sits between its two
+// measured cases: on a 2048 x 2048 output (one tile per CU) it beats the four-wave blocks by
+// 10-15 %, on a 4096 x 2048 output (two rounds against one round of two blocks per CU) it
+// loses by 25 %.
+enum WgradShape { kW256x256, kW128x128, kW256x192, kW192x256, kW128x128k2 };
 
 inline WgradShape pick_wgrad_shape(int64_t I, int64_t J) {
   struct Cand {
@@ -634,6 +770,7 @@ inline WgradShape pick_wgrad_shape(int64_t I, int64_t J) {
   const Cand cands[] = {
       {kW256x256, 256, 256, 1, 1.00, true},
       {kW128x128, 128, 128, 2, 0.85, false},
+      {kW128x128k2, 128, 128, 1, 0.60, false},
       {kW256x192, 256, 192, 1, 0.97, true},
       {kW192x256, 192, 256, 1, 0.97, true},
   };
@@ -668,6 +805,18 @@ puro_status launch(GemmKernel k, const void* A, const float* sA, const void* B, 
   return launch_status();
 }
 
+template <class C>
+puro_status launch_k2(GemmKernel k, const void* A, const float* sA, const void* B,
+                      const float* sB, void* Cout, int64_t I, int64_t J, int64_t L,
+                      int accumulate, void* stream) {
+  const int64_t blocks = ((I + C::BM - 1) / C::BM) * ((J + C::BN - 1) / C::BN);
+  if (blocks > INT32_MAX) return PURO_ERR_SHAPE;
+  hipLaunchKernelGGL(k, dim3(static_cast<uint32_t>(blocks)), dim3(2 * C::kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint8_t*>(A), sA,
+                     static_cast<const uint8_t*>(B), sB, Cout, I, J, L, accumulate);
+  return launch_status();
+}
+
 // Kernels of one scale rule.
 template <bool kPow2>
 struct Kernels;
@@ -685,6 +834,7 @@ struct Kernels<false> {
   static constexpr GemmKernel dg_b = gemm_dgrad_256x256, dg_s = gemm_dgrad_128x128;
   static constexpr GemmKernel wg_b = gemm_wgrad_256x256, wg_s = gemm_wgrad_128x128;
   static constexpr GemmKernel wg_w = gemm_wgrad_256x192, wg_t = gemm_wgrad_192x256;
+  static constexpr GemmKernel wg_k2 = gemm_wgrad_128x128_k2;
 };
 template <>
 struct Kernels<true> {
@@ -700,6 +850,7 @@ struct Kernels<true> {
   static constexpr GemmKernel dg_b = gemm_dgrad_256x256_pow2, dg_s = gemm_dgrad_128x128_pow2;
   static constexpr GemmKernel wg_b = gemm_wgrad_256x256_pow2, wg_s = gemm_wgrad_128x128_pow2;
   static constexpr GemmKernel wg_w = gemm_wgrad_256x192_pow2, wg_t = gemm_wgrad_192x256_pow2;
+  static constexpr GemmKernel wg_k2 = gemm_wgrad_128x128_k2_pow2;
 };
 
 template <bool kPow2>
@@ -763,6 +914,9 @@ puro_status gemm_wgrad(const void* dytq, const float* sdyt, const void* xtq, con
     case kW192x256:
       return launch<typename Ks::WgT>(Ks::wg_t, dytq, sdyt, xtq, sxt, dw, N, K, M, accumulate,
                                       stream);
+    case kW128x128k2:
+      return launch_k2<typename Ks::WgS>(Ks::wg_k2, dytq, sdyt, xtq, sxt, dw, N, K, M,
+                                         accumulate, stream);
     default:
       return launch<typename Ks::WgS>(Ks::wg_s, dytq, sdyt, xtq, sxt, dw, N, K, M, accumulate,
                                       stream);

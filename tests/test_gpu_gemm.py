@@ -128,10 +128,13 @@ def test_wgrad_accumulate(puro, oracle, pow2):
 
 
 # Weight-gradient outputs chosen so that each tile shape the library picks from is used on a
-# 256-CU part: 128x128 (rows not a multiple of 256; and a 4096 x 2048 output), 256x192 (a
-# 2048 x 4608 output: one round instead of two), 192x256 (a 12288 x 2048 output: two rounds of
-# 512 tiles); sampled output rows, overwrite and accumulate.
-WGRAD_SHAPES = [(256, 128, 384), (256, 4096, 2048), (256, 2048, 4608), (256, 12288, 2048)]
+# 256-CU part: the split-reduction 128x128 tile (a 128 x 384 output; a 2048 x 2048 output over
+# 9 chunks, so one group multiplies out one chunk more than the other), the four-wave 128x128
+# tile (a 4096 x 2048 output: one round of two blocks per CU), 256x192 (a 2048 x 4608 output:
+# one round instead of two), 192x256 (a 12288 x 2048 output: two rounds of 512 tiles); sampled
+# output rows, overwrite and accumulate.
+WGRAD_SHAPES = [(256, 128, 384), (1152, 2048, 2048), (256, 4096, 2048), (256, 2048, 4608),
+                (256, 12288, 2048)]
 
 
 @pytest.mark.parametrize("M,N,K", WGRAD_SHAPES)

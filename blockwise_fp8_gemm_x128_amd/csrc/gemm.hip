@@ -22,12 +22,17 @@
 // chunks through a two-stage LDS pipeline: while chunk c is multiplied out of one stage, chunk
 // c+1 (A tile, B tile and the A/B scale rows) streams into the other stage with
 // buffer_load_dwordx4 ... lds, which writes LDS directly (no VGPR staging, no ds_write). One
-// barrier per chunk separates "stage landed" from "stage free". Each 128-byte row of a staged
-// operand keeps its eight 16-byte pieces XOR-permuted (piece p at slot p ^ swz(row)). The two
-// swizzles below were chosen by measurement on MI355X (SQ_LDS_BANK_CONFLICT of each candidate's
-// exact read pattern): both the 16-byte fragment reads (16 rows x 4 lane groups) and the 8-byte
-// transposed reads (4 lane groups x 8 rows x 2 halves) run with no bank-conflict cycles, where
-// the unswizzled layout costs 12 and 14 cycles per read instruction.
+// barrier per chunk separates "stage landed" from "stage free". In the 8-wave tiles only half of
+// the waves issue a given chunk's DMA, the halves alternating by chunk parity: the issue is
+// held up by the CU's memory pipeline (a 256x256 chunk is 64 KB), and the two waves sharing a
+// SIMD are in different halves, so one of them keeps the matrix core busy meanwhile.
+//
+// Each 128-byte row of a staged operand keeps its eight 16-byte pieces XOR-permuted (piece p at
+// slot p ^ swz(row)). The two swizzles below were chosen by measurement on MI355X
+// (SQ_LDS_BANK_CONFLICT of each candidate's exact read pattern): both the 16-byte fragment reads
+// (16 rows x 4 lane groups) and the 8-byte transposed reads (4 lane groups x 8 rows x 2 halves)
+// run with no bank-conflict cycles, where the unswizzled layout costs 12 and 14 cycles per read
+// instruction.
 //
 // Block order: workgroups are dispatched round-robin over the 8 XCDs, so the block id is first
 // remapped so that consecutive tiles run on one XCD (sharing that XCD's L2), and tiles are
@@ -139,15 +144,20 @@ __device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, ld
 
 template <class C>
 struct Loader {
-  static constexpr int kAInstr = C::BM / 8 / C::kWaves;  // DMA instructions per wave, A tile
-  static constexpr int kBInstr = C::BN / 8 / C::kWaves;  // and B tile
+  // 8-wave tiles alternate the DMA between the two halves of the block by chunk parity (waves w
+  // and w + 4 share a SIMD, so while one of them is held up feeding the memory pipeline the
+  // other keeps the matrix core busy); 4-wave tiles spread every chunk over all their waves.
+  static constexpr bool kPingPong = C::kWaves == 8;
+  static constexpr int kIssuers = kPingPong ? C::kWaves / 2 : C::kWaves;
+  static constexpr int kAInstr = C::BM / 8 / kIssuers;  // DMA instructions per issuing wave, A
+  static constexpr int kBInstr = C::BN / 8 / kIssuers;  // and B tile
 
-  // Instruction k of wave w copies staged rows [8q, 8q+8), q = w + kWaves*k; lane l takes row
-  // 8q + l/8 and physical piece l%8, i.e. logical piece (l%8) ^ swz(row). For row-major operands
-  // swz_rows(8q + l/8) depends only on l and on q & 1 = w & 1 (kWaves is even), so all of a
-  // lane's instructions share one per-lane offset; for slabs swz_slab depends on k as well and
-  // each instruction gets its own. Row and chunk offsets are wave-uniform (scalar offset or
-  // resource base).
+  // Instruction k of issuing wave w copies staged rows [8q, 8q+8), q = w + kIssuers*k; lane l
+  // takes row 8q + l/8 and physical piece l%8, i.e. logical piece (l%8) ^ swz(row). For
+  // row-major operands swz_rows(8q + l/8) depends only on l and on q & 1 = w & 1 (kIssuers is
+  // even), so all of a lane's instructions share one per-lane offset; for slabs swz_slab depends
+  // on k as well and each instruction gets its own. Row and chunk offsets are wave-uniform
+  // (scalar offset or resource base).
   const uint8_t* A;
   const uint8_t* B;
   const float* sA;
@@ -161,15 +171,17 @@ struct Loader {
   int64_t sb_block_step;
 
   __device__ __forceinline__ void init(int wn) {
-    static_assert(C::kWaves % 2 == 0, "row-major DMA swizzle assumes an even wave count");
+    static_assert(kIssuers % 2 == 0, "row-major DMA swizzle assumes an even issuer count");
+    static_assert((C::BM / 8) % kIssuers == 0 && (C::BN / 8) % kIssuers == 0, "even DMA split");
+    const int w = kPingPong ? wave % kIssuers : wave;  // this wave's place among the issuers
     const int r8 = lane >> 3, p8 = lane & 7;
-    const int xr = swz_rows(8 * wave + r8);  // = swz_rows(8q + r8) for every instruction k
+    const int xr = swz_rows(8 * w + r8);  // = swz_rows(8q + r8) for every instruction k
     ra = make_rsrc(A + i0 * L, (I - i0) * L);
     a_voff = static_cast<uint32_t>(r8 * L + ((p8 ^ xr) << 4));
     if (C::kBTrans) {
 #pragma unroll
       for (int k = 0; k < kBInstr; ++k) {
-        const int rr = 8 * ((wave + C::kWaves * k) & 15) + r8;  // row inside its slab
+        const int rr = 8 * ((w + kIssuers * k) & 15) + r8;  // row inside its slab
         bt_voff[k] = static_cast<uint32_t>(r8 * J + ((p8 ^ swz_slab(rr)) << 4));
       }
     } else {
@@ -187,11 +199,56 @@ struct Loader {
     }
   }
 
-  // Enqueue chunk c into `stage` (every wave issues its share; DMA writes LDS directly).
+  // Enqueue chunk c into `stage`: the issuing half of an 8-wave block (every wave of a 4-wave
+  // block) issues its share; the DMA writes LDS directly.
   __device__ __forceinline__ void issue(lds_u8* stage, int64_t c) const {
+    if constexpr (kPingPong) {
+      if (wave / kIssuers == static_cast<int>(c & 1)) issue_as(stage, c, wave % kIssuers);
+    } else {
+      // The same share written out with the wave index itself: routed through issue_as, the
+      // compiler merged the two scale loads of the 4-wave weight-gradient kernel into one with
+      // a selected source and that kernel ran 7-9 % slower (measured on MI355X).
+#pragma unroll
+      for (int k = 0; k < kAInstr; ++k) {
+        const int q = wave + C::kWaves * k;
+        dma16(ra, a_voff, static_cast<uint32_t>(8 * q * L + c * kChunk),
+              stage + C::kAOff + 8 * q * kChunk);
+      }
+      if (C::kBTrans) {
+        // staged B = BN/128 slabs of 128 reduction rows x 128 columns; slab s holds columns
+        // j0 + 128 s .. +127 and its row rr is reduction row rr of the chunk
+        const uint8_t* base = B + c * kChunk * J + j0;
+        const rsrc_t rbc = make_rsrc(base, (L - c * kChunk) * J - j0);
+#pragma unroll
+        for (int k = 0; k < kBInstr; ++k) {
+          const int q = wave + C::kWaves * k;
+          const int sl = q >> 4, qq = q & 15;
+          dma16(rbc, bt_voff[k], static_cast<uint32_t>(8 * qq * J + 128 * sl),
+                stage + C::kBOff + 8 * q * kChunk);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < kBInstr; ++k) {
+          const int q = wave + C::kWaves * k;
+          dma16(rb, b_voff, static_cast<uint32_t>(8 * q * L + c * kChunk),
+                stage + C::kBOff + 8 * q * kChunk);
+        }
+      }
+      // scale rows: all 64 lanes (no divergence); lanes past the tile's rows read zeros
+      if (wave == 0)
+        dma16(make_rsrc(sA + c * I + i0, imin64(I - i0, C::BM) * 4), 16 * lane, 0,
+              stage + C::kSAOff);
+      if (C::kPerColScale && wave == (1 % C::kWaves))
+        dma16(make_rsrc(sB + c * J + j0, imin64(J - j0, C::BN) * 4), 16 * lane, 0,
+              stage + C::kSBOff);
+    }
+  }
+
+  // The share of issuing wave w.
+  __device__ __forceinline__ void issue_as(lds_u8* stage, int64_t c, int w) const {
 #pragma unroll
     for (int k = 0; k < kAInstr; ++k) {
-      const int q = wave + C::kWaves * k;
+      const int q = w + kIssuers * k;
       dma16(ra, a_voff, static_cast<uint32_t>(8 * q * L + c * kChunk),
             stage + C::kAOff + 8 * q * kChunk);
     }
@@ -202,7 +259,7 @@ struct Loader {
       const rsrc_t rbc = make_rsrc(base, (L - c * kChunk) * J - j0);
 #pragma unroll
       for (int k = 0; k < kBInstr; ++k) {
-        const int q = wave + C::kWaves * k;
+        const int q = w + kIssuers * k;
         const int sl = q >> 4, qq = q & 15;
         dma16(rbc, bt_voff[k], static_cast<uint32_t>(8 * qq * J + 128 * sl),
               stage + C::kBOff + 8 * q * kChunk);
@@ -210,16 +267,16 @@ struct Loader {
     } else {
 #pragma unroll
       for (int k = 0; k < kBInstr; ++k) {
-        const int q = wave + C::kWaves * k;
+        const int q = w + kIssuers * k;
         dma16(rb, b_voff, static_cast<uint32_t>(8 * q * L + c * kChunk),
               stage + C::kBOff + 8 * q * kChunk);
       }
     }
     // scale rows: all 64 lanes (no divergence); lanes past the tile's rows read zeros
-    if (wave == 0)
+    if (w == 0)
       dma16(make_rsrc(sA + c * I + i0, imin64(I - i0, C::BM) * 4), 16 * lane, 0,
             stage + C::kSAOff);
-    if (C::kPerColScale && wave == (1 % C::kWaves))
+    if (C::kPerColScale && w == 1)
       dma16(make_rsrc(sB + c * J + j0, imin64(J - j0, C::BN) * 4), 16 * lane, 0,
             stage + C::kSBOff);
   }

@@ -25,7 +25,9 @@
 // barrier per chunk separates "stage landed" from "stage free". In the 8-wave tiles only half of
 // the waves issue a given chunk's DMA, the halves alternating by chunk parity: the issue is
 // held up by the CU's memory pipeline (a 256x256 chunk is 64 KB), and the two waves sharing a
-// SIMD are in different halves, so one of them keeps the matrix core busy meanwhile.
+// SIMD are in different halves, so one of them keeps the matrix core busy meanwhile. The
+// issuing half sends its A rows right after the barrier and its B rows after the chunk's first
+// row block of products.
 //
 // Each 128-byte row of a staged operand keeps its eight 16-byte pieces XOR-permuted (piece p at
 // slot p ^ swz(row)). The two swizzles below were chosen by measurement on MI355X
@@ -199,15 +201,18 @@ struct Loader {
     }
   }
 
-  // Enqueue chunk c into `stage`: the issuing half of an 8-wave block (every wave of a 4-wave
-  // block) issues its share; the DMA writes LDS directly.
+  // Enqueue chunk c into `stage` (the DMA writes LDS directly). A 4-wave block issues all of it
+  // here, every wave its share. In an 8-wave block only the issuing half takes part, and here
+  // only its A rows and scale rows: its B rows follow from issue_second, after the first row
+  // block's products, so that the issuing waves never stall on 16 loads in a row (measured: with
+  // one burst, the long-reduction data gradient ran 6 % slower in the model step).
   __device__ __forceinline__ void issue(lds_u8* stage, int64_t c) const {
     if constexpr (kPingPong) {
-      if (wave / kIssuers == static_cast<int>(c & 1)) issue_as(stage, c, wave % kIssuers);
+      if (wave / kIssuers == static_cast<int>(c & 1)) issue_as_a(stage, c, wave % kIssuers);
     } else {
-      // The same share written out with the wave index itself: routed through issue_as, the
-      // compiler merged the two scale loads of the 4-wave weight-gradient kernel into one with
-      // a selected source and that kernel ran 7-9 % slower (measured on MI355X).
+      // The same share written out with the wave index itself: routed through the issuing-wave
+      // functions below, the compiler merged the two scale loads of the 4-wave weight-gradient
+      // kernel into one with a selected source and that kernel ran 7-9 % slower (MI355X).
 #pragma unroll
       for (int k = 0; k < kAInstr; ++k) {
         const int q = wave + C::kWaves * k;
@@ -244,14 +249,31 @@ struct Loader {
     }
   }
 
-  // The share of issuing wave w.
-  __device__ __forceinline__ void issue_as(lds_u8* stage, int64_t c, int w) const {
+  // Second part of chunk c's DMA in an 8-wave block: the issuing half's B rows.
+  __device__ __forceinline__ void issue_second(lds_u8* stage, int64_t c) const {
+    if constexpr (kPingPong) {
+      if (wave / kIssuers == static_cast<int>(c & 1)) issue_as_b(stage, c, wave % kIssuers);
+    }
+  }
+
+  // The share of issuing wave w (of kIssuers) in an 8-wave block: the A rows with the scale rows,
+  // and the B rows.
+  __device__ __forceinline__ void issue_as_a(lds_u8* stage, int64_t c, int w) const {
 #pragma unroll
     for (int k = 0; k < kAInstr; ++k) {
       const int q = w + kIssuers * k;
       dma16(ra, a_voff, static_cast<uint32_t>(8 * q * L + c * kChunk),
             stage + C::kAOff + 8 * q * kChunk);
     }
+    // scale rows: all 64 lanes (no divergence); lanes past the tile's rows read zeros
+    if (w == 0)
+      dma16(make_rsrc(sA + c * I + i0, imin64(I - i0, C::BM) * 4), 16 * lane, 0,
+            stage + C::kSAOff);
+    if (C::kPerColScale && w == 1)
+      dma16(make_rsrc(sB + c * J + j0, imin64(J - j0, C::BN) * 4), 16 * lane, 0,
+            stage + C::kSBOff);
+  }
+  __device__ __forceinline__ void issue_as_b(lds_u8* stage, int64_t c, int w) const {
     if (C::kBTrans) {
       // staged B = BN/128 slabs of 128 reduction rows x 128 columns; slab s holds columns
       // j0 + 128 s .. +127 and its row rr is reduction row rr of the chunk
@@ -272,14 +294,8 @@ struct Loader {
               stage + C::kBOff + 8 * q * kChunk);
       }
     }
-    // scale rows: all 64 lanes (no divergence); lanes past the tile's rows read zeros
-    if (w == 0)
-      dma16(make_rsrc(sA + c * I + i0, imin64(I - i0, C::BM) * 4), 16 * lane, 0,
-            stage + C::kSAOff);
-    if (C::kPerColScale && w == 1)
-      dma16(make_rsrc(sB + c * J + j0, imin64(J - j0, C::BN) * 4), 16 * lane, 0,
-            stage + C::kSBOff);
   }
+
 };
 
 // Per-lane LDS byte offsets of this wave's fragment reads, fixed for the whole kernel. Every
@@ -375,10 +391,16 @@ struct ChunkState {
   float sa_cur, sa_next, sa_prev;
 };
 
-template <class C, int k>
+// Hook a chunk runs before its second row block (the second part of the next chunk's DMA in
+// 8-wave tiles); by default nothing.
+struct NoMid {
+  __device__ __forceinline__ void operator()() const {}
+};
+
+template <class C, int k, class Mid>
 __device__ __forceinline__ void chunk_step(const lds_u8* stage, const FragOffsets<C>& o,
                                            ChunkState<C>& st, float sb_blk,
-                                           v4f (&acc)[C::MI][C::NJ]) {
+                                           v4f (&acc)[C::MI][C::NJ], const Mid& mid) {
   constexpr int kTiles = C::MI * C::NJ;
   if constexpr (k < kTiles + C::NJ) {
     constexpr int mi = k / C::NJ, nj = k % C::NJ;
@@ -388,6 +410,7 @@ __device__ __forceinline__ void chunk_step(const lds_u8* stage, const FragOffset
         st.af_next = frag_a<C, mi + 1>(stage, o);
         st.sa_next = scale_a<C, mi + 1>(stage, o);
       }
+      if constexpr (k == C::NJ) mid();
       st.p[k % kWin] = mfma_fp8(st.bf[nj], st.af_cur);
     }
     if constexpr (k >= C::NJ) {
@@ -409,7 +432,7 @@ __device__ __forceinline__ void chunk_step(const lds_u8* stage, const FragOffset
         st.sa_cur = st.sa_next;
       }
     }
-    chunk_step<C, k + 1>(stage, o, st, sb_blk, acc);
+    chunk_step<C, k + 1>(stage, o, st, sb_blk, acc, mid);
   }
 }
 
@@ -427,15 +450,15 @@ __device__ __forceinline__ void load_bf(const lds_u8* stage, const FragOffsets<C
 }
 
 // One 128-wide reduction chunk out of a landed stage.
-template <class C>
+template <class C, class Mid = NoMid>
 __device__ __forceinline__ void compute_chunk(const lds_u8* stage, float sb_blk,
                                               const FragOffsets<C>& o,
-                                              v4f (&acc)[C::MI][C::NJ]) {
+                                              v4f (&acc)[C::MI][C::NJ], const Mid& mid = Mid()) {
   ChunkState<C> st;
   load_bf<C, 0>(stage, o, st, sb_blk);
   st.af_cur = frag_a<C, 0>(stage, o);
   st.sa_cur = scale_a<C, 0>(stage, o);
-  chunk_step<C, 0>(stage, o, st, sb_blk, acc);
+  chunk_step<C, 0>(stage, o, st, sb_blk, acc, mid);
 }
 
 // ------------------------------------------------------------------ power-of-two scales
@@ -473,15 +496,17 @@ __device__ __forceinline__ void load_bf_pow2(const lds_u8* stage, const FragOffs
 
 // Tile k = mi * NJ + nj; the next row block's A fragment and scale are fetched at the start of
 // each row block, as in the promoted path.
-template <class C, int k>
+template <class C, int k, class Mid>
 __device__ __forceinline__ void pow2_step(const lds_u8* stage, const FragOffsets<C>& o,
-                                          Pow2State<C>& st, v4f (&acc)[C::MI][C::NJ]) {
+                                          Pow2State<C>& st, v4f (&acc)[C::MI][C::NJ],
+                                          const Mid& mid) {
   if constexpr (k < C::MI * C::NJ) {
     constexpr int mi = k / C::NJ, nj = k % C::NJ;
     if constexpr (nj == 0 && mi + 1 < C::MI) {
       st.af_next = frag_a<C, mi + 1>(stage, o);
       st.ea_next = e8m0(scale_a<C, mi + 1>(stage, o));
     }
+    if constexpr (k == C::NJ) mid();
     acc[mi][nj] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
         st.bf[nj], st.af_cur, acc[mi][nj], 0, 0, 0, st.eb[nj], 0, st.ea_cur);
     __builtin_amdgcn_sched_barrier(0);
@@ -489,19 +514,20 @@ __device__ __forceinline__ void pow2_step(const lds_u8* stage, const FragOffsets
       st.af_cur = st.af_next;
       st.ea_cur = st.ea_next;
     }
-    pow2_step<C, k + 1>(stage, o, st, acc);
+    pow2_step<C, k + 1>(stage, o, st, acc, mid);
   }
 }
 
-template <class C>
+template <class C, class Mid = NoMid>
 __device__ __forceinline__ void compute_chunk_pow2(const lds_u8* stage, float sb_blk,
                                                    const FragOffsets<C>& o,
-                                                   v4f (&acc)[C::MI][C::NJ]) {
+                                                   v4f (&acc)[C::MI][C::NJ],
+                                                   const Mid& mid = Mid()) {
   Pow2State<C> st;
   load_bf_pow2<C, 0>(stage, o, st, e8m0(sb_blk));
   st.af_cur = frag_a<C, 0>(stage, o);
   st.ea_cur = e8m0(scale_a<C, 0>(stage, o));
-  pow2_step<C, 0>(stage, o, st, acc);
+  pow2_step<C, 0>(stage, o, st, acc, mid);
   // Pin the accumulators at the end of the chunk: without this, IR-level sinking moves the
   // chunk's instructions past the next barrier, keeping all its fragments live (spills).
 #pragma unroll
@@ -596,7 +622,10 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A,
 #pragma unroll
     for (int nj = 0; nj < C::NJ; ++nj) acc[mi][nj] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  if (nk > 0) ld.issue(stage0, 0);
+  if (nk > 0) {
+    ld.issue(stage0, 0);
+    ld.issue_second(stage0, 0);
+  }
   float sb_next = (!C::kPerColScale && nk > 0) ? ld.sb_block[0] : 0.0f;
 
   // Chunks go in pairs (stage0 then stage1) so that each stage is a distinct LDS object; an odd
@@ -611,10 +640,13 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A,
       ld.issue(nxt, c + 1);
       if (!C::kPerColScale) sb_next = ld.sb_block[(c + 1) * ld.sb_block_step];
     }
+    auto mid = [&]() {  // runs before the chunk's second row block
+      if (c + 1 < nk) ld.issue_second(nxt, c + 1);
+    };
     if constexpr (C::kPow2)
-      compute_chunk_pow2<C>(cur, sb, fo, acc);
+      compute_chunk_pow2<C>(cur, sb, fo, acc, mid);
     else
-      compute_chunk<C>(cur, sb, fo, acc);
+      compute_chunk<C>(cur, sb, fo, acc, mid);
   };
   int64_t c = 0;
   for (; c + 1 < nk; c += 2) {

@@ -162,6 +162,29 @@ def test_big_tiles_with_ragged_edge(puro, oracle, pow2):
     run_dgrad(puro, oracle, dy, w2, rows=rows, what="dgrad ragged big tiles", pow2=pow2)
 
 
+# The 8-wave tiles alternate each chunk's DMA between the two halves of the block by chunk
+# parity, and the last chunk of an odd count takes its own path through the pipeline: odd
+# chunk counts (1, 3, 9) on shapes that use the 256x256 (forward, data gradient) and 256x192
+# (weight gradient, 2048 x 6144 output) tiles.
+@pytest.mark.parametrize("chunks", [1, 3, 9])
+@pytest.mark.parametrize("pow2", [False, True])
+def test_big_tiles_odd_chunks(puro, oracle, chunks, pow2):
+    R = 128 * chunks
+    seed = 130 + chunks
+    x = synth.randn_bf16((4096, R), 1.0, seed)
+    w = synth.randn_bf16((4096, R), 0.02, seed + 1)
+    run_fwd(puro, oracle, x, w, rows=sample_rows(4096, 12, seed), what=f"fwd {chunks} chunks",
+            pow2=pow2)
+    dy = synth.randn_bf16((4096, R), 1e-3, seed + 2)
+    w2 = synth.randn_bf16((R, 4096), 0.02, seed + 3)
+    run_dgrad(puro, oracle, dy, w2, rows=sample_rows(4096, 12, seed + 4),
+              what=f"dgrad {chunks} chunks", pow2=pow2)
+    xw = synth.randn_bf16((R, 6144), 1.0, seed + 5)
+    dyw = synth.randn_bf16((R, 2048), 1e-3, seed + 6)
+    run_wgrad(puro, oracle, dyw, xw, rows=sample_rows(2048, 8, seed + 7),
+              what=f"wgrad {chunks} chunks", pow2=pow2)
+
+
 def test_zero_reduction(puro):
     say("zero reduction")
     xq = torch.empty((256, 0), dtype=torch.uint8, device="cuda")

@@ -185,6 +185,31 @@ def test_big_tiles_odd_chunks(puro, oracle, chunks, pow2):
               what=f"wgrad {chunks} chunks", pow2=pow2)
 
 
+# Seeded random shapes (every dimension a multiple of 128): small ones, which the 128x128 and
+# split-reduction kernels take, and large outputs with short reductions, which the 8-wave
+# kernels take; all three GEMMs against the oracle on sampled rows, both scale rules.
+def _random_shapes():
+    rng = np.random.default_rng(2024)
+    small = [tuple(int(v) * 128 for v in rng.integers(1, 17, size=3)) for _ in range(5)]
+    large = [(int(rng.integers(24, 65)) * 128, int(rng.integers(24, 65)) * 128,
+              int(rng.integers(1, 10)) * 128) for _ in range(4)]
+    return small + large
+
+
+@pytest.mark.parametrize("M,N,K", _random_shapes())
+@pytest.mark.parametrize("pow2", [False, True])
+def test_random_shapes(puro, oracle, M, N, K, pow2):
+    seed = 7 * M + 5 * N + 3 * K + int(pow2)
+    x = synth.randn_bf16((M, K), 1.0, seed)
+    w = synth.randn_bf16((N, K), 0.02, seed + 1)
+    dy = synth.randn_bf16((M, N), 1e-3, seed + 2)
+    run_fwd(puro, oracle, x, w, rows=sample_rows(M, 10, seed), what="random fwd", pow2=pow2)
+    run_dgrad(puro, oracle, dy, w, rows=sample_rows(M, 10, seed + 3), what="random dgrad",
+              pow2=pow2)
+    run_wgrad(puro, oracle, dy, x, rows=sample_rows(N, 8, seed + 4), what="random wgrad",
+              pow2=pow2)
+
+
 def test_zero_reduction(puro):
     say("zero reduction")
     xq = torch.empty((256, 0), dtype=torch.uint8, device="cuda")

@@ -88,6 +88,24 @@ def test_shapes(puro, oracle, shape, std, seed, pow2):
     check_all_three(puro, oracle, x, f"randn std={std}", pow2=pow2)
 
 
+# Seeded random shapes with log-normal magnitudes (|x| spread over ~40 binary orders within a
+# tensor, signs random): every group lands at its own scale, and many elements encode to e4m3
+# subnormals or flush to signed zero; bytes and scales bit-exact against the oracle.
+def _lognormal(shape, seed):
+    g = torch.Generator().manual_seed(seed)
+    mag = torch.exp(torch.randn(shape, generator=g) * 4.0)
+    sign = torch.where(torch.rand(shape, generator=g) < 0.5, -1.0, 1.0)
+    return (sign * mag).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("case", range(6))
+@pytest.mark.parametrize("pow2", [False, True])
+def test_random_lognormal(puro, oracle, case, pow2):
+    rng = np.random.default_rng(300 + case)
+    shape = (int(rng.integers(1, 13)) * 128, int(rng.integers(1, 13)) * 128)
+    check_all_three(puro, oracle, _lognormal(shape, 400 + case), f"lognormal {shape}", pow2=pow2)
+
+
 @pytest.mark.parametrize("pow2", [False, True])
 def test_special_values(puro, oracle, pow2):
     rows = []

@@ -17,6 +17,22 @@
 namespace puro {
 namespace {
 
+// 16 bytes of an input each quantiser reads exactly once, loaded non-temporally so that the
+// bf16 source does not displace, in L2 and the memory-side cache, the e4m3 copies the GEMMs
+// read next. Measured on the model step: the quantisers and the following data gradient got
+// faster, the step 2.2 % (the dual quantiser alone with plain loads elsewhere made the weight
+// quantiser slower; every quantiser together is what pays).
+__device__ __forceinline__ uint4 load_once16(const uint16_t* p) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  uint4 v;
+  v.x = t[0];
+  v.y = t[1];
+  v.z = t[2];
+  v.w = t[3];
+  return v;
+}
+
 // ------------------------------------------------------------------ 1x128 row groups
 // One group = 128 consecutive bf16 of a row = 16 lanes x 8 elements. A 256-thread block holds
 // 16 groups per pass and makes 4 passes, so it covers 64 consecutive rows of one 128-column
@@ -40,7 +56,7 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t* __
 #pragma unroll
   for (int p = 0; p < kActPasses; ++p) {
     const int64_t row = rb * kActRowsPerBlock + p * 16 + seg;
-    v[p] = *reinterpret_cast<const uint4*>(x + row * cols + c * 128 + l16 * 8);
+    v[p] = load_once16(x + row * cols + c * 128 + l16 * 8);
   }
 #pragma unroll
   for (int p = 0; p < kActPasses; ++p) {
@@ -79,7 +95,7 @@ __device__ __forceinline__ void quant_w_block(const uint16_t* __restrict__ w, in
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int64_t row = bi * 128 + r0 + 16 * i;
-    v[i] = *reinterpret_cast<const uint4*>(w + row * k + bj * 128 + col);
+    v[i] = load_once16(w + row * k + bj * 128 + col);
   }
   float m = 0.0f;
 #pragma unroll
@@ -168,7 +184,7 @@ __global__ __launch_bounds__(256) void quant_transpose_kernel(const uint16_t* __
     uint4 v[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      v[i] = *reinterpret_cast<const uint4*>(x + (m0 + r + 32 * i) * cols + c0 + c8 * 8);
+      v[i] = load_once16(x + (m0 + r + 32 * i) * cols + c0 + c8 * 8);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       uint32_t* dst = tile + (r + 32 * i) * kTrPitch + c8 * 4;
@@ -245,7 +261,7 @@ __global__ __launch_bounds__(512) void quant_dual_1x128_kernel(
     uint4 v[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p)
-      v[p] = *reinterpret_cast<const uint4*>(x + (m0 + 32 * p + seg) * cols + c0 + l16 * 8);
+      v[p] = load_once16(x + (m0 + 32 * p + seg) * cols + c0 + l16 * 8);
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int r = 32 * p + seg;

@@ -19,6 +19,15 @@
 namespace puro {
 namespace {
 
+// 16 bytes of an input read exactly once (the update direction, the gradient), loaded
+// non-temporally so that it does not displace the masters, which the projected step reads twice
+// (measured: the projected step 2 % faster).
+__device__ __forceinline__ float4 load_once4f(const float4* p) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return make_float4(t[0], t[1], t[2], t[3]);
+}
+
 constexpr int kOptThreads = 256;
 constexpr int kOptMaxBlocks = PURO_OPT_MAX_BLOCKS;
 // workspace layout: [kOptMaxBlocks] double partial sums
@@ -59,7 +68,7 @@ __global__ __launch_bounds__(kOptThreads) void sumsq_kernel(const float* src,
        i += int64_t(gridDim.x) * kOptThreads) {
     float4 a = s4[i];
     if constexpr (kUpdate) {
-      const float4 b = u4[i];
+      const float4 b = load_once4f(u4 + i);
       a.x = fmaf(-lr, b.x, a.x);
       a.y = fmaf(-lr, b.y, a.y);
       a.z = fmaf(-lr, b.z, a.z);
@@ -149,7 +158,7 @@ __global__ __launch_bounds__(kOptThreads) void adamw_kernel(float* __restrict__ 
   for (int64_t i = int64_t(blockIdx.x) * kOptThreads + threadIdx.x; i < n4;
        i += int64_t(gridDim.x) * kOptThreads) {
     float4 pp = p4[i], mm = m4[i], vv = v4[i];
-    const float4 gg = g4[i];
+    const float4 gg = load_once4f(g4 + i);
     adamw_one(pp.x, gg.x, mm.x, vv.x, a);
     adamw_one(pp.y, gg.y, mm.y, vv.y, a);
     adamw_one(pp.z, gg.z, mm.z, vv.z, a);

@@ -159,93 +159,19 @@ __global__ __launch_bounds__(256) void quant_w_128x128_group_kernel(const WGroup
   quant_w_block<kPow2>(g.w[i], g.n[i], g.k[i], g.q[i], g.s[i], b - g.first[i], wave_max);
 }
 
-// ------------------------------------------------------------------ transposed 1x128 groups
-// Tile = 128 rows x 64 columns of x (one group per column). Load: 8 lanes per 128 B row
-// segment, 4 passes of 32 rows, staged in LDS as dwords (2 bf16) with a 33-dword row pitch.
-// Compute: wave w owns tile columns [16w, 16w+16) as 8 column pairs; lane = 8*g + pair holds
-// rows [16g, 16g+16) of its pair, so a column's amax is an 8-lane reduction and a column's
-// 128 output bytes are written by 8 lanes as one contiguous 128 B segment.
-constexpr int kTrPitch = 33;  // dwords per staged row (32 data + 1 pad)
-
-template <bool kPow2>
-__global__ __launch_bounds__(256) void quant_transpose_kernel(const uint16_t* __restrict__ x,
-                                                              int64_t rows, int64_t cols,
-                                                              uint8_t* __restrict__ qt,
-                                                              float* __restrict__ st) {
-  __shared__ uint32_t tile[128 * kTrPitch];
-  const int64_t cblocks = cols >> 6;
-  const int64_t cb = blockIdx.x % cblocks;
-  const int64_t mb = blockIdx.x / cblocks;
-  const int64_t m0 = mb * 128, c0 = cb * 64;
-  const int t = threadIdx.x;
-
-  {
-    const int r = t >> 3, c8 = t & 7;
-    uint4 v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      v[i] = load_once16(x + (m0 + r + 32 * i) * cols + c0 + c8 * 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t* dst = tile + (r + 32 * i) * kTrPitch + c8 * 4;
-      dst[0] = v[i].x;
-      dst[1] = v[i].y;
-      dst[2] = v[i].z;
-      dst[3] = v[i].w;
-    }
-  }
-  __syncthreads();
-
-  const int w = t >> 6, lane = t & 63;
-  const int pair = lane & 7, g = lane >> 3;
-  const int dc = w * 8 + pair;  // dword column: tile columns 2*dc, 2*dc+1
-  uint32_t d[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) d[i] = tile[(16 * g + i) * kTrPitch + dc];
-  float m0v = 0.0f, m1v = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    m0v = fmaxf(m0v, __builtin_fabsf(bf16_lo(d[i])));
-    m1v = fmaxf(m1v, __builtin_fabsf(bf16_hi(d[i])));
-  }
-#pragma unroll
-  for (int off = 8; off < 64; off <<= 1) {
-    m0v = fmaxf(m0v, __shfl_xor(m0v, off, 64));
-    m1v = fmaxf(m1v, __shfl_xor(m1v, off, 64));
-  }
-  float s0, r0, s1, r1;
-  scale_rule<kPow2>(m0v, s0, r0);
-  scale_rule<kPow2>(m1v, s1, r1);
-  uint4 o0, o1;
-  o0.x = e4m3x4(bf16_lo(d[0]) * r0, bf16_lo(d[1]) * r0, bf16_lo(d[2]) * r0, bf16_lo(d[3]) * r0);
-  o0.y = e4m3x4(bf16_lo(d[4]) * r0, bf16_lo(d[5]) * r0, bf16_lo(d[6]) * r0, bf16_lo(d[7]) * r0);
-  o0.z = e4m3x4(bf16_lo(d[8]) * r0, bf16_lo(d[9]) * r0, bf16_lo(d[10]) * r0,
-                bf16_lo(d[11]) * r0);
-  o0.w = e4m3x4(bf16_lo(d[12]) * r0, bf16_lo(d[13]) * r0, bf16_lo(d[14]) * r0,
-                bf16_lo(d[15]) * r0);
-  o1.x = e4m3x4(bf16_hi(d[0]) * r1, bf16_hi(d[1]) * r1, bf16_hi(d[2]) * r1, bf16_hi(d[3]) * r1);
-  o1.y = e4m3x4(bf16_hi(d[4]) * r1, bf16_hi(d[5]) * r1, bf16_hi(d[6]) * r1, bf16_hi(d[7]) * r1);
-  o1.z = e4m3x4(bf16_hi(d[8]) * r1, bf16_hi(d[9]) * r1, bf16_hi(d[10]) * r1,
-                bf16_hi(d[11]) * r1);
-  o1.w = e4m3x4(bf16_hi(d[12]) * r1, bf16_hi(d[13]) * r1, bf16_hi(d[14]) * r1,
-                bf16_hi(d[15]) * r1);
-  const int64_t col = c0 + 2 * dc;
-  *reinterpret_cast<uint4*>(qt + col * rows + m0 + 16 * g) = o0;
-  *reinterpret_cast<uint4*>(qt + (col + 1) * rows + m0 + 16 * g) = o1;
-  if (g == 0) *reinterpret_cast<float2*>(st + mb * cols + col) = make_float2(s0, s1);
-}
-
-// ------------------------------------------------------------------ both orientations at once
+// ------------------------------------------------------------------ column groups, and both at once
 // One 512-thread block per 128x128 tile of x, read from HBM once. Pass 1: 16 lanes per 256 B
-// row, 4 passes of 32 rows; each row's 128 values form one row group (quantised and stored from
-// registers) and are also staged in LDS as dwords with a 65-dword row pitch. Pass 2: as in the
-// transposed quantiser, 8 lanes per column pair, each holding 16 rows, so a column's amax is an
-// 8-lane reduction and its 128 output bytes are one contiguous 128 B segment; the 8 waves cover
-// the 64 column pairs in one round. (Eight waves per block rather than four: twice the waves
-// per CU for the same 33 KB of LDS, measured 2 % faster over the model's shapes.)
+// row, 4 passes of 32 rows; the tile is staged in LDS as dwords with a 65-dword row pitch and,
+// with kRows, each row's 128 values also form one row group, quantised and stored from
+// registers. Pass 2: 8 lanes per column pair, each holding 16 rows, so a column's amax is an
+// 8-lane reduction and its 128 output bytes (the transposed copy) are one contiguous 128 B
+// segment; the 8 waves cover the 64 column pairs in one round. (Eight waves per block rather
+// than four: twice the waves per CU for the same 33 KB of LDS, measured 2 % faster over the
+// model's shapes.) Without kRows this is the transposed quantiser on its own: it replaced a
+// 128x64-tile kernel whose 128 B row segments read HBM less efficiently.
 constexpr int kDualPitch = 65;  // dwords per staged row (64 data + 1 pad)
 
-template <bool kPow2>
+template <bool kPow2, bool kRows>
 __global__ __launch_bounds__(512) void quant_dual_1x128_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, uint8_t* __restrict__ q,
     float* __restrict__ s, uint8_t* __restrict__ qt, float* __restrict__ st) {
@@ -270,6 +196,7 @@ __global__ __launch_bounds__(512) void quant_dual_1x128_kernel(
       dst[1] = v[p].y;
       dst[2] = v[p].z;
       dst[3] = v[p].w;
+      if constexpr (!kRows) continue;
       const float f[8] = {bf16_lo(v[p].x), bf16_hi(v[p].x), bf16_lo(v[p].y), bf16_hi(v[p].y),
                           bf16_lo(v[p].z), bf16_hi(v[p].z), bf16_lo(v[p].w), bf16_hi(v[p].w)};
       float m = 0.0f;
@@ -371,12 +298,12 @@ puro_status quant_transpose(const void* x, int64_t rows, int64_t cols, void* qt,
   PURO_TRY(check_ptr(qt, empty));
   PURO_TRY(check_ptr(st, empty));
   if (empty) return PURO_OK;
-  const int64_t blocks = (rows / 128) * (cols / 64);
+  const int64_t blocks = (rows / 128) * (cols / 128);
   if (blocks > INT32_MAX) return PURO_ERR_SHAPE;
-  hipLaunchKernelGGL(quant_transpose_kernel<kPow2>, dim3(static_cast<uint32_t>(blocks)),
-                     dim3(256), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const uint16_t*>(x), rows, cols, static_cast<uint8_t*>(qt),
-                     st);
+  const auto kernel = quant_dual_1x128_kernel<kPow2, false>;  // column groups only
+  hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(512), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint16_t*>(x), rows, cols, nullptr, nullptr,
+                     static_cast<uint8_t*>(qt), st);
   return launch_status();
 }
 
@@ -393,8 +320,8 @@ puro_status quant_dual_1x128(const void* x, int64_t rows, int64_t cols, void* q,
   if (empty) return PURO_OK;
   const int64_t blocks = (rows / 128) * (cols / 128);
   if (blocks > INT32_MAX) return PURO_ERR_SHAPE;
-  hipLaunchKernelGGL(quant_dual_1x128_kernel<kPow2>, dim3(static_cast<uint32_t>(blocks)),
-                     dim3(512), 0, static_cast<hipStream_t>(stream),
+  const auto kernel = quant_dual_1x128_kernel<kPow2, true>;
+  hipLaunchKernelGGL(kernel, dim3(static_cast<uint32_t>(blocks)), dim3(512), 0, static_cast<hipStream_t>(stream),
                      static_cast<const uint16_t*>(x), rows, cols, static_cast<uint8_t*>(q), s,
                      static_cast<uint8_t*>(qt), st);
   return launch_status();

@@ -713,12 +713,19 @@ __device__ __forceinline__ void gemm_body_k2(const uint8_t* __restrict__ A,
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const int64_t cn = 2 * (p + 1) + g;
-    if (cn < nk) ld.issue(nxt + goff, cn);
+    // group 0 issues its next chunk right away, group 1 before its second row block, so that
+    // the two waves sharing a SIMD do not both feed the memory pipeline at once
+    if (g == 0 && cn < nk) ld.issue(nxt + goff, cn);
+    auto mid = [&]() {
+      if (g == 1 && cn < nk) ld.issue(nxt + goff, cn);
+    };
     if (2 * p + g < nk) {
       if constexpr (C::kPow2)
-        compute_chunk_pow2<C>(cur + goff, 0.0f, fo, acc);
+        compute_chunk_pow2<C>(cur + goff, 0.0f, fo, acc, mid);
       else
-        compute_chunk<C>(cur + goff, 0.0f, fo, acc);
+        compute_chunk<C>(cur + goff, 0.0f, fo, acc, mid);
+    } else {
+      mid();
     }
   };
   const int64_t steps = (nk + 1) / 2;

@@ -36,6 +36,11 @@
 // run with no bank-conflict cycles, where the unswizzled layout costs 12 and 14 cycles per read
 // instruction.
 //
+// Epilogue: the fragment layout leaves four adjacent results per lane, so stores written
+// straight from the accumulators cover a quarter (bf16) or half (fp32) cache line per row.
+// Waves 64 columns wide therefore restage their block through LDS (the freed stages) and
+// store whole rows, 16 bytes per lane.
+//
 // Block order: workgroups are dispatched round-robin over the 8 XCDs, so the block id is first
 // remapped so that consecutive tiles run on one XCD (sharing that XCD's L2), and tiles are
 // walked in bands of 8 tile-rows, column by column, so concurrently running tiles share A and B
@@ -584,6 +589,80 @@ __device__ __forceinline__ void store_tile(const v4f (&acc)[C::MI][C::NJ], void*
   }
 }
 
+// Epilogue through LDS, for waves 64 columns wide. Stored straight from the fragments, each
+// instruction writes 16 rows x 4 columns, a quarter (bf16) or half (fp32) of a cache line per
+// row, and on MI355X the output stores of a round of bf16 tiles took about 9 us, a quarter of a
+// 16-chunk tile's time. Instead each wave converts its block into a private LDS region and then
+// writes whole rows, 16 bytes per lane, so every store covers full lines (measured: 2-4 us less
+// per round of tiles). The regions reuse the stages once every wave has passed the barrier at
+// the top (the last chunk has been read); the 16-byte units of a row are XOR-swizzled by the
+// row's low bits so that neither the fragment writes nor the row reads conflict on LDS banks.
+// A stage holds the regions of half the waves; an fp32 block that does not fit goes in two
+// passes over its rows.
+template <class C>
+__device__ __forceinline__ void store_tile_lds(const v4f (&acc)[C::MI][C::NJ], void* Cout,
+                                               int64_t I, int64_t J, int64_t i0, int64_t j0,
+                                               int wm, int wn, int wave, int lane, int accumulate,
+                                               lds_u8* stage0, lds_u8* stage1) {
+  constexpr int kElt = C::kOutF32 ? 4 : 2;
+  constexpr int kRowBytes = kElt * C::WN;
+  constexpr int kUnits = kRowBytes / 16;  // 16-byte units per row: 8 (bf16) or 16 (fp32)
+  constexpr int kPerStage = C::kWaves / 2;
+  constexpr int kPasses = kPerStage * C::WM * kRowBytes <= C::kStageBytes ? 1 : 2;
+  constexpr int kPassMI = C::MI / kPasses;
+  constexpr int kRows = 16 * kPassMI;  // rows of the block per pass
+  constexpr int kRowsPerStore = 64 / kUnits;
+  static_assert(C::WN == 64 && C::MI % kPasses == 0, "64-column waves, whole fragments a pass");
+  static_assert(kPerStage * kRows * kRowBytes <= C::kStageBytes, "regions fit the stages");
+  __syncthreads();
+  const int64_t r0 = i0 + wm * C::WM, q0 = j0 + wn * C::WN;
+  if (r0 >= I || q0 >= J) return;  // this wave lies in the invalid half of an edge tile
+  lds_u8* region = (wave < kPerStage ? stage0 : stage1) + (wave % kPerStage) * kRows * kRowBytes;
+  const int G = lane >> 4, r16 = lane & 15;
+  const int lr = lane / kUnits, lu = lane % kUnits;
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+#pragma unroll
+    for (int m = 0; m < kPassMI; ++m) {
+      const int row = 16 * m + r16;
+#pragma unroll
+      for (int nj = 0; nj < C::NJ; ++nj) {
+        const v4f v = acc[pass * kPassMI + m][nj];
+        if constexpr (C::kOutF32) {
+          const int unit = 4 * nj + G;
+          *reinterpret_cast<lds_v4f*>(region + row * kRowBytes + 16 * (unit ^ (row & 7))) = v;
+        } else {
+          const int unit = 2 * nj + (G >> 1);
+          v2i packed;
+          packed[0] = static_cast<int>(pack_bf16x2(v[0], v[1]));
+          packed[1] = static_cast<int>(pack_bf16x2(v[2], v[3]));
+          *reinterpret_cast<lds_v2i*>(region + row * kRowBytes + 16 * (unit ^ (row & 7)) +
+                                      8 * (G & 1)) = packed;
+        }
+      }
+    }
+    // the reads below take other lanes' writes: wait for them, and keep the compiler from
+    // moving any LDS access across
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int p = 0; p < kRows / kRowsPerStore; ++p) {
+      const int row = kRowsPerStore * p + lr;
+      const v4i raw = *reinterpret_cast<const lds_v4i_t*>(region + row * kRowBytes +
+                                                          16 * (lu ^ (row & 7)));
+      const int64_t grow = r0 + pass * kRows + row;
+      if constexpr (C::kOutF32) {
+        v4f* out = reinterpret_cast<v4f*>(static_cast<float*>(Cout) + grow * J + q0 + 4 * lu);
+        const v4f v = __builtin_bit_cast(v4f, raw);
+        *out = accumulate ? *out + v : v;
+      } else {
+        *reinterpret_cast<v4i*>(static_cast<uint16_t*>(Cout) + grow * J + q0 + 8 * lu) = raw;
+      }
+    }
+    // the next pass overwrites the region: keep its writes after these reads
+    if (pass + 1 < kPasses) asm volatile("" ::: "memory");
+  }
+}
+
 template <class C>
 __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A,
                                           const float* __restrict__ sA,
@@ -655,7 +734,10 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A,
   }
   if (c < nk) half(stage0, stage1, c);
 
-  store_tile<C>(acc, Cout, I, J, i0, j0, wm, wn, lane, accumulate);
+  if constexpr (C::WN == 64)
+    store_tile_lds<C>(acc, Cout, I, J, i0, j0, wm, wn, wave, lane, accumulate, stage0, stage1);
+  else
+    store_tile<C>(acc, Cout, I, J, i0, j0, wm, wn, lane, accumulate);
 }
 
 // Weight gradient of a small output with the reduction split inside the block: two groups of

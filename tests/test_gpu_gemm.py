@@ -131,10 +131,11 @@ def test_wgrad_accumulate(puro, oracle, pow2):
 # 256-CU part: the split-reduction 128x128 tile (a 128 x 384 output; a 2048 x 2048 output over
 # 9 chunks, so one group multiplies out one chunk more than the other), the four-wave 128x128
 # tile (a 4096 x 2048 output: one round of two blocks per CU), 256x192 (a 2048 x 4608 output:
-# one round instead of two), 192x256 (a 12288 x 2048 output: two rounds of 512 tiles); sampled
+# one round instead of two), 192x256 (a 12288 x 2048 output: two rounds of 512 tiles), 256x256
+# (a 4096 x 4096 output: one round; its fp32 epilogue goes through LDS in two passes); sampled
 # output rows, overwrite and accumulate.
 WGRAD_SHAPES = [(256, 128, 384), (1152, 2048, 2048), (256, 4096, 2048), (256, 2048, 4608),
-                (256, 12288, 2048)]
+                (256, 12288, 2048), (256, 4096, 4096)]
 
 
 @pytest.mark.parametrize("M,N,K", WGRAD_SHAPES)
@@ -150,15 +151,16 @@ def test_wgrad_tile_shapes(puro, oracle, M, N, K, acc, pow2):
 
 @pytest.mark.parametrize("pow2", [False, True])
 def test_big_tiles_with_ragged_edge(puro, oracle, pow2):
-    # 16512 = 64.5 x 256 rows: enough 256x256 tiles for the big-tile kernels, whose last tile
-    # row is half outside the output; the sampled rows include that half tile.
-    M, N, K = 16512, 1024, 256
+    # 16512 = 64.5 x 256 rows and 1152 = 4.5 x 256 columns: enough 256x256 tiles for the
+    # big-tile kernels, whose last tile row and last tile column are half outside the output
+    # (there half of the waves store nothing); the sampled rows include the half tile row.
+    M, N, K = 16512, 1152, 256
     x = synth.randn_bf16((M, K), 1.0, 111)
     w = synth.randn_bf16((N, K), 0.02, 112)
     dy = synth.randn_bf16((M, N), 1e-3, 113)
     rows = np.unique(np.concatenate([sample_rows(M, 16, 114), np.arange(M - 130, M)]))
     run_fwd(puro, oracle, x, w, rows=rows, what="fwd ragged big tiles", pow2=pow2)
-    w2 = synth.randn_bf16((N, 1024), 0.02, 115)
+    w2 = synth.randn_bf16((N, 1152), 0.02, 115)
     run_dgrad(puro, oracle, dy, w2, rows=rows, what="dgrad ragged big tiles", pow2=pow2)
 
 

@@ -38,8 +38,8 @@
 //
 // Epilogue: the fragment layout leaves four adjacent results per lane, so stores written
 // straight from the accumulators cover a quarter (bf16) or half (fp32) cache line per row.
-// Waves 64 columns wide therefore restage their block through LDS (the freed stages) and
-// store whole rows, 16 bytes per lane.
+// Waves 64 columns wide therefore restage their block through LDS (the stage the last chunk did
+// not use) and store whole rows, 16 bytes per lane.
 //
 // Block order: workgroups are dispatched round-robin over the 8 XCDs, so the block id is first
 // remapped so that consecutive tiles run on one XCD (sharing that XCD's L2), and tiles are
@@ -594,30 +594,34 @@ __device__ __forceinline__ void store_tile(const v4f (&acc)[C::MI][C::NJ], void*
 // row, and on MI355X the output stores of a round of bf16 tiles took about 9 us, a quarter of a
 // 16-chunk tile's time. Instead each wave converts its block into a private LDS region and then
 // writes whole rows, 16 bytes per lane, so every store covers full lines (measured: 2-4 us less
-// per round of tiles). The regions reuse the stages once every wave has passed the barrier at
-// the top (the last chunk has been read); the 16-byte units of a row are XOR-swizzled by the
-// row's low bits so that neither the fragment writes nor the row reads conflict on LDS banks.
-// A stage holds the regions of half the waves; an fp32 block that does not fit goes in two
-// passes over its rows.
+// per round of tiles). The regions lie in the stage the last chunk did not use: every wave has
+// passed the barrier in front of that chunk, which came after all reads of the other stage, and
+// no DMA is issued after it, so no further barrier is needed and each wave starts its stores
+// as soon as its own products are done (measured: 0.8 % on the step against restaging into both
+// stages behind one more barrier). One stage holds every wave's region for a share of its rows,
+// so the block goes in 1-6 passes over its rows; the 16-byte units of a row are XOR-swizzled by
+// the row's low bits so that the row reads do not conflict on LDS banks.
 template <class C>
 __device__ __forceinline__ void store_tile_lds(const v4f (&acc)[C::MI][C::NJ], void* Cout,
                                                int64_t I, int64_t J, int64_t i0, int64_t j0,
                                                int wm, int wn, int wave, int lane, int accumulate,
-                                               lds_u8* stage0, lds_u8* stage1) {
+                                               lds_u8* free_stage) {
   constexpr int kElt = C::kOutF32 ? 4 : 2;
   constexpr int kRowBytes = kElt * C::WN;
   constexpr int kUnits = kRowBytes / 16;  // 16-byte units per row: 8 (bf16) or 16 (fp32)
-  constexpr int kPerStage = C::kWaves / 2;
-  constexpr int kPasses = kPerStage * C::WM * kRowBytes <= C::kStageBytes ? 1 : 2;
+  constexpr int kBlockBytes = C::kWaves * C::WM * kRowBytes;
+  constexpr int kPasses = kBlockBytes <= C::kStageBytes                          ? 1
+                          : kBlockBytes <= 2 * C::kStageBytes && C::MI % 2 == 0 ? 2
+                          : kBlockBytes <= 4 * C::kStageBytes && C::MI % 4 == 0 ? 4
+                                                                                : C::MI;
   constexpr int kPassMI = C::MI / kPasses;
   constexpr int kRows = 16 * kPassMI;  // rows of the block per pass
   constexpr int kRowsPerStore = 64 / kUnits;
   static_assert(C::WN == 64 && C::MI % kPasses == 0, "64-column waves, whole fragments a pass");
-  static_assert(kPerStage * kRows * kRowBytes <= C::kStageBytes, "regions fit the stages");
-  __syncthreads();
+  static_assert(C::kWaves * kRows * kRowBytes <= C::kStageBytes, "regions fit one stage");
   const int64_t r0 = i0 + wm * C::WM, q0 = j0 + wn * C::WN;
   if (r0 >= I || q0 >= J) return;  // this wave lies in the invalid half of an edge tile
-  lds_u8* region = (wave < kPerStage ? stage0 : stage1) + (wave % kPerStage) * kRows * kRowBytes;
+  lds_u8* region = free_stage + wave * kRows * kRowBytes;
   const int G = lane >> 4, r16 = lane & 15;
   const int lr = lane / kUnits, lu = lane % kUnits;
 #pragma unroll
@@ -659,7 +663,7 @@ __device__ __forceinline__ void store_tile_lds(const v4f (&acc)[C::MI][C::NJ], v
       }
     }
     // the next pass overwrites the region: keep its writes after these reads
-    if (pass + 1 < kPasses) asm volatile("" ::: "memory");
+    if (pass + 1 < kPasses) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   }
 }
 
@@ -735,7 +739,8 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A,
   if (c < nk) half(stage0, stage1, c);
 
   if constexpr (C::WN == 64)
-    store_tile_lds<C>(acc, Cout, I, J, i0, j0, wm, wn, wave, lane, accumulate, stage0, stage1);
+    store_tile_lds<C>(acc, Cout, I, J, i0, j0, wm, wn, wave, lane, accumulate,
+                      (nk & 1) ? stage1 : stage0);
   else
     store_tile<C>(acc, Cout, I, J, i0, j0, wm, wn, lane, accumulate);
 }

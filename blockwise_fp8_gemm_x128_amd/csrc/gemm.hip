@@ -659,7 +659,11 @@ __device__ __forceinline__ void store_tile_lds(const v4f (&acc)[C::MI][C::NJ], v
         const v4f v = __builtin_bit_cast(v4f, raw);
         *out = accumulate ? *out + v : v;
       } else {
-        *reinterpret_cast<v4i*>(static_cast<uint16_t*>(Cout) + grow * J + q0 + 8 * lu) = raw;
+        // Non-temporal: the bf16 output is not read again by this step's next kernels, and
+        // keeping it out of L2 and the memory-side cache leaves room for the operands and codes
+        // they do read (measured on the step: 39.9 -> 39.3 ms, the quantisers 3-7 % faster).
+        __builtin_nontemporal_store(
+            raw, reinterpret_cast<v4i*>(static_cast<uint16_t*>(Cout) + grow * J + q0 + 8 * lu));
       }
     }
     // the next pass overwrites the region: keep its writes after these reads

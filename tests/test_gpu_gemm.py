@@ -164,6 +164,37 @@ def test_big_tiles_with_ragged_edge(puro, oracle, pow2):
     run_dgrad(puro, oracle, dy, w2, rows=rows, what="dgrad ragged big tiles", pow2=pow2)
 
 
+@pytest.mark.parametrize("pow2", [False, True])
+def test_big_tile_edges_write_nothing_outside(puro, pow2):
+    # The ragged 256x256 forward and data-gradient outputs are written into the front of a
+    # buffer followed by 256 sentinel rows: the waves of the half-outside tiles (last tile row
+    # and last tile column) must store nothing, so the sentinels survive, and the output equals
+    # that of a call into a buffer of its own.
+    M, N, K = 16512, 1152, 256
+    sentinel = 0x7FC1  # a bf16 NaN the kernels never produce
+    x = synth.randn_bf16((M, K), 1.0, 121).cuda()
+    w = synth.randn_bf16((N, K), 0.02, 122).cuda()
+    dy = synth.randn_bf16((M, N), 1e-3, 123).cuda()
+    w2 = synth.randn_bf16((N, 1152), 0.02, 124).cuda()
+    xq, sx = fn(puro, "puro_quant_act_1x128", pow2)(x)
+    wq, sw = fn(puro, "puro_quant_w_128x128", pow2)(w)
+    dyq, sdy = fn(puro, "puro_quant_act_1x128", pow2)(dy)
+    w2q, sw2 = fn(puro, "puro_quant_w_128x128", pow2)(w2)
+    for what, call, cols in (
+            ("fwd", lambda out: fn(puro, "puro_fp8_gemm_fwd", pow2)(xq, sx, wq, sw, out), N),
+            ("dgrad", lambda out: fn(puro, "puro_fp8_gemm_dgrad", pow2)(dyq, sdy, w2q, sw2, out),
+             1152)):
+        say("edges", what, "M, cols =", M, cols, "pow2" if pow2 else "")
+        buf = torch.empty((M + 256, cols), dtype=torch.bfloat16, device="cuda")
+        buf.view(torch.int16).fill_(sentinel)
+        call(buf[:M])
+        ref = call(None)
+        torch.cuda.synchronize()
+        tail = buf[M:].view(torch.int16)
+        assert bool((tail == sentinel).all()), f"{what}: a store landed past the output"
+        assert torch.equal(buf[:M].view(torch.int16), ref.view(torch.int16)), what
+
+
 # The 8-wave tiles alternate each chunk's DMA between the two halves of the block by chunk
 # parity, and the last chunk of an odd count takes its own path through the pipeline: odd
 # chunk counts (1, 3, 9) on shapes that use the 256x256 (forward, data gradient) and 256x192

@@ -3,10 +3,11 @@
 // and both 1x128 orientations from one read.
 //
 // Method: Paper walkthrough: Puro-2B (ta-paperlens.web.app), section "Lever 2: use blockwise
-// FP8 from step zero" — scales are taken per local group, activations and their gradients in
-// groups of 128 along the reduction dimension and weights in 128x128 blocks. Number formats
-// and rounding as stated in include/puro.h. Every kernel is instantiated for two scale rules:
-// amax/448 (the reading of the pages) and the power of two at or above it (a library option).
+// FP8 from step zero" — one fp32 scale per local group: a 1x128 run along the consuming GEMM's
+// reduction dimension for activations and activation gradients, a 128x128 block for weights.
+// Number formats and rounding as stated in include/puro.h. Every kernel is instantiated for two
+// scale rules: amax/448 (the reading of the pages) and the power of two at or above it (a
+// library option).
 //
 // All of them are HBM-bound: each bf16 element is read once (2 B) and each of its E4M3 codes
 // written once (1 B per copy), plus one fp32 scale per group. Loads are 16 B per lane and every

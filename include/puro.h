@@ -104,7 +104,7 @@ puro_status puro_quant_transpose(const void* x, int64_t rows, int64_t cols, void
 
 /* Both 1x128 orientations of one bf16 matrix from a single read of it: the row groups of
  * puro_quant_act_1x128 and the column groups of puro_quant_transpose, bit for bit the same
- * outputs as those two calls. The same passage defines both (groups of 128 along the reduction
+ * outputs as those two calls. The same passage defines both (1x128 runs along the reduction
  * dimension of the GEMM that consumes each copy): an activation X feeds the forward GEMM
  * (reduction over its columns) and the weight-gradient GEMM (reduction over its rows), and so
  * does an output gradient dY for the data-gradient and weight-gradient GEMMs.

@@ -8,8 +8,8 @@
  * What is computed, and where it is stated:
  *   Paper walkthrough: Puro-2B (ta-paperlens.web.app), section
  *   "Lever 2: use blockwise FP8 from step zero": only the linear-layer GEMMs run in FP8;
- *   scales are per local group — activations and their gradients in groups of 128 along the
- *   reduction dimension, weights in 128x128 blocks; master weights stay BF16/FP32.
+ *   one scale per local group — a 1x128 run along the GEMM's reduction dimension for
+ *   activations and activation gradients, a 128x128 block for weights; masters stay BF16/FP32.
  *   PuRo-2B news post (jj-blog.pages.dev), driver-hack section, training-recipe paragraph:
  *   blockwise FP8 only for the linear-layer GEMMs, masters BF16/FP32, sequence 4096.
  *

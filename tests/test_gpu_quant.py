@@ -201,3 +201,50 @@ def test_empty(puro):
     assert q.shape == (0, 256) and s.shape == (2, 0) and qt.shape == (256, 0) and st.shape == (0, 256)
     q, s, qt, st = puro.puro_quant_dual_1x128_pow2(x)
     assert q.shape == (0, 256) and s.shape == (2, 0) and qt.shape == (256, 0) and st.shape == (0, 256)
+
+
+@pytest.mark.parametrize("fname,pow2", [("quant_hand.txt", False), ("quant_pow2_hand.txt", True)])
+def test_hand_golden_groups(puro, fname, pow2):
+    # the hand-derived golden groups (including the two that tell the payload factor
+    # fl32(x * fl32(448/amax)) from x/s and x * fl32(1/s)), straight against their stated codes
+    # and scales, as row groups and, through the transpose, as column groups
+    from helpers import read_quant_hand
+    cases = read_quant_hand(fname)
+    grid = np.zeros((128, 128), np.float32)
+    want_q = np.zeros((128, 128), np.uint8)
+    want_s = np.ones(128, np.float32)
+    for r, c in enumerate(cases):
+        for i, v in c["values"].items():
+            grid[r, i] = v
+        for i, code in c["codes"].items():
+            want_q[r, i] = code
+        want_s[r] = c["scale"]
+    x = torch.tensor(grid).to(torch.bfloat16)
+    assert np.array_equal(x.float().numpy().view(np.uint32), grid.view(np.uint32))
+    say("hand golden groups", fname, len(cases))
+    q, s = gpu_act(puro, x, pow2)
+    assert np.array_equal(q, want_q), np.argwhere(q != want_q)[:5].tolist()
+    assert np.array_equal(s[0].view(np.uint32), want_s.view(np.uint32))
+    qt, st = gpu_tr(puro, x.t().contiguous(), pow2)
+    assert np.array_equal(qt, want_q) and np.array_equal(st[0].view(np.uint32), want_s.view(np.uint32))
+
+
+def test_pow2_subnormal_amax(puro, oracle):
+    # power-of-two groups whose largest magnitude is itself a bf16 subnormal: the exponent is
+    # raised to -127 (scale = fp32 subnormal 0x00400000) and the payload is x * 2^127, exact
+    z = np.zeros(128, np.float32)
+    rows = []
+    r = z.copy(); r[0] = 2.0 ** -127; r[1] = -(2.0 ** -130); r[2] = 2.0 ** -133; rows.append(r)
+    r = z.copy(); r[9] = -(2.0 ** -133); rows.append(r)
+    r = z.copy(); r[:8] = 3 * 2.0 ** -133 * np.arange(1, 9); r[100] = -(2.0 ** -126) * 0.5; rows.append(r)
+    r = z.copy(); r[::5] = -(2.0 ** -128); r[1::5] = 2.0 ** -131; rows.append(r)
+    grid = np.zeros((128, 128), np.float32)
+    grid[:len(rows)] = np.stack(rows)
+    grid[64:64 + len(rows)] = -np.stack(rows)
+    x = torch.tensor(grid).to(torch.bfloat16)
+    xf = x.float().numpy()
+    amax = np.abs(xf).max(axis=1)
+    assert np.all(amax[:len(rows)] < 2.0 ** -126) and np.all(amax[:len(rows)] > 0)
+    check_all_three(puro, oracle, x, "pow2 subnormal amax", pow2=True)
+    q, s = gpu_act(puro, x, True)
+    assert np.all(s[0, :len(rows)].view(np.uint32) == 0x00400000)

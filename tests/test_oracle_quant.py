@@ -8,7 +8,8 @@ import numpy as np
 import pytest
 import torch
 
-from helpers import (bf16_bits_to_f32, f32_to_bf16_bits, read_quant_hand, torch_e4m3_decode)
+from helpers import (bf16_bits_to_f32, f32_to_bf16_bits, read_quant_hand, torch_e4m3_decode,
+                     torch_e4m3_encode)
 
 
 def _group_from_case(case):
@@ -151,3 +152,26 @@ def test_transpose_equals_act_of_transpose(oracle):
     qa, sa = oracle.quant_act_1x128(np.ascontiguousarray(x.T))
     assert np.array_equal(qt, qa)
     assert np.array_equal(st, sa)
+
+
+@pytest.mark.parametrize("std,seed", [(1.0, 21), (0.02, 22), (1e-3, 23)])
+def test_payload_against_numpy_and_torch_cast(oracle, std, seed):
+    # The standard rule rebuilt from library arithmetic on 16384 seeded groups: numpy's fp32
+    # division and multiply (each one correctly rounded operation) for the factor and the scaled
+    # value, torch's float8_e4m3fn cast for the encoding. A few percent of N(0,1) groups hold an
+    # element whose exact scaled value is an E4M3 midpoint, where a different factor rule
+    # (x/s, x * fl32(1/s)) would give another byte.
+    x = _rand_bf16((16384, 128), seed, std)
+    xf = bf16_bits_to_f32(x)
+    amax = np.max(np.abs(xf), axis=1, keepdims=True)
+    r = np.where(amax > 0, np.float32(448.0) / np.where(amax > 0, amax, 1), np.float32(1.0))
+    t = np.clip((xf * r.astype(np.float32)).astype(np.float32), -448.0, 448.0)
+    want = torch_e4m3_encode(t)
+    q, s = oracle.quant_act_1x128(x)
+    assert np.array_equal(q, want)
+    assert np.array_equal(s[0], np.where(amax[:, 0] > 0, amax[:, 0] / np.float32(448.0), 1.0).astype(np.float32))
+    # the midpoint cases are present in this sample: the alternatives differ somewhere
+    s32 = (amax / np.float32(448.0)).astype(np.float32)
+    alt_d = torch_e4m3_encode(np.clip((xf / s32).astype(np.float32), -448, 448))
+    alt_i = torch_e4m3_encode(np.clip((xf * (np.float32(1.0) / s32)).astype(np.float32), -448, 448))
+    assert np.any(alt_d != want) and np.any(alt_i != want)

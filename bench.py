@@ -118,6 +118,7 @@ class Stack:
 
         self.persist = []
         self.weights = []
+        self.linears = []  # per (layer, linear): its name, sizes and per-layer tensors
         wq_ops, fwd, bwd = [], [], []
         for layer in range(layers):
             group_w, group_q, group_s = [], [], []
@@ -141,6 +142,9 @@ class Stack:
                 sdyt = buf(("sdyt", li), (M // 128, N), torch.float32)
                 self.persist += [x, w, dy, wq, sw, dw]
                 self.weights.append((w, dw))  # bf16 copy of the master, and its gradient
+                rec = {"layer": layer, "li": li, "name": name, "K": K, "N": N, "x": x, "w": w,
+                       "dy": dy, "wq": wq, "sw": sw, "dw": dw}
+                self.linears.append(rec)
                 f = 2.0 * M * N * K
                 group_w.append(w)
                 group_q.append(wq)
@@ -158,6 +162,7 @@ class Stack:
                     xtq = torch.empty((K, M), dtype=torch.uint8, device=dev)
                     sxt = torch.empty((M // 128, K), dtype=torch.float32, device=dev)
                     self.persist += [xtq, sxt]
+                    rec.update(xtq=xtq, sxt=sxt)
                     lf += [Op("quant_dual_1x128" + sfx, 0.0, M * K * B_DUAL,
                               *prep("puro_quant_dual_1x128", x, M, K, xq, sx, xtq, sxt)),
                            g_fwd]

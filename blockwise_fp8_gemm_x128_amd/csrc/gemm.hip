@@ -53,6 +53,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "dma_offsets.hpp"
 
 namespace puro {
 namespace {
@@ -132,9 +133,10 @@ __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b) {
 }
 
 // 16 bytes per lane from global memory straight into LDS through a buffer resource: lane i's
-// bytes (at base + voff_i + soff) land at lds_dst + 16 * i (lds_dst is wave-uniform). Offsets
-// at or beyond the resource's byte count read as zero, which covers the invalid half of edge
-// tiles without any clamping.
+// bytes (at base + voff_i) land at lds_dst + 16 * i (lds_dst is wave-uniform). The whole offset
+// is the per-lane one and the scalar offset is 0, so the range check sees the row (and column)
+// each lane addresses: offsets at or beyond the resource's byte count read as zero, which covers
+// the invalid part of edge tiles without clamping and without reading past a tensor's end.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;  // raw, untyped 32-bit-offset buffer (gfx9 family)
 
@@ -144,9 +146,18 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
                                            kRsrcWord3);
 }
 
-__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, lds_u8* lds_dst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 16, static_cast<int>(voff),
-                                           static_cast<int>(soff), 0, 0);
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, lds_u8* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 16, static_cast<int>(voff), 0,
+                                           0, 0);
+}
+
+// A chunk's lane offset: the lane part plus the chunk's column offset, hidden from the
+// optimiser so that it does not keep one hoisted register per load of the chunk (each load adds
+// its wave-uniform row-group offset to this one register instead).
+__device__ __forceinline__ uint32_t chunk_lane_offset(uint32_t lane_part, int64_t c) {
+  uint32_t v = lane_part + static_cast<uint32_t>(c * 128);
+  asm volatile("" : "+v"(v));
+  return v;
 }
 
 template <class C>
@@ -162,9 +173,9 @@ struct Loader {
   // Instruction k of issuing wave w copies staged rows [8q, 8q+8), q = w + kIssuers*k; lane l
   // takes row 8q + l/8 and physical piece l%8, i.e. logical piece (l%8) ^ swz(row). For
   // row-major operands swz_rows(8q + l/8) depends only on l and on q & 1 = w & 1 (kIssuers is
-  // even), so all of a lane's instructions share one per-lane offset; for slabs swz_slab depends
-  // on k as well and each instruction gets its own. Row and chunk offsets are wave-uniform
-  // (scalar offset or resource base).
+  // even), so all of a lane's instructions share one lane part of the offset, to which each
+  // load adds its wave-uniform row-group and chunk part; for slabs swz_slab depends on k as well
+  // and each instruction keeps its own whole offset (the chunk is in the resource base).
   const uint8_t* A;
   const uint8_t* B;
   const float* sA;
@@ -184,16 +195,17 @@ struct Loader {
     const int r8 = lane >> 3, p8 = lane & 7;
     const int xr = swz_rows(8 * w + r8);  // = swz_rows(8q + r8) for every instruction k
     ra = make_rsrc(A + i0 * L, (I - i0) * L);
-    a_voff = static_cast<uint32_t>(r8 * L + ((p8 ^ xr) << 4));
+    a_voff = dma::rows_lane(r8, p8 ^ xr, L);
     if (C::kBTrans) {
 #pragma unroll
       for (int k = 0; k < kBInstr; ++k) {
-        const int rr = 8 * ((w + kIssuers * k) & 15) + r8;  // row inside its slab
-        bt_voff[k] = static_cast<uint32_t>(r8 * J + ((p8 ^ swz_slab(rr)) << 4));
+        const int q = w + kIssuers * k;
+        const int rr = 8 * (q & 15) + r8;  // row inside its slab
+        bt_voff[k] = dma::slab_lane(q, r8, p8 ^ swz_slab(rr), J);
       }
     } else {
       rb = make_rsrc(B + j0 * L, (J - j0) * L);
-      b_voff = static_cast<uint32_t>(r8 * L + ((p8 ^ xr) << 4));
+      b_voff = dma::rows_lane(r8, p8 ^ xr, L);
     }
     const int64_t jb = imin64(j0 + (wave % C::WAVES_N) * C::WN, J - 1) / 128;
     (void)wn;
@@ -218,11 +230,11 @@ struct Loader {
       // The same share written out with the wave index itself: routed through the issuing-wave
       // functions below, the compiler merged the two scale loads of the 4-wave weight-gradient
       // kernel into one with a selected source and that kernel ran 7-9 % slower (MI355X).
+      const uint32_t av = chunk_lane_offset(a_voff, c);
 #pragma unroll
       for (int k = 0; k < kAInstr; ++k) {
         const int q = wave + C::kWaves * k;
-        dma16(ra, a_voff, static_cast<uint32_t>(8 * q * L + c * kChunk),
-              stage + C::kAOff + 8 * q * kChunk);
+        dma16(ra, av + dma::rows_group(q, L, 0), stage + C::kAOff + 8 * q * kChunk);
       }
       if (C::kBTrans) {
         // staged B = BN/128 slabs of 128 reduction rows x 128 columns; slab s holds columns
@@ -232,24 +244,22 @@ struct Loader {
 #pragma unroll
         for (int k = 0; k < kBInstr; ++k) {
           const int q = wave + C::kWaves * k;
-          const int sl = q >> 4, qq = q & 15;
-          dma16(rbc, bt_voff[k], static_cast<uint32_t>(8 * qq * J + 128 * sl),
-                stage + C::kBOff + 8 * q * kChunk);
+          dma16(rbc, bt_voff[k], stage + C::kBOff + 8 * q * kChunk);
         }
       } else {
+        const uint32_t bv = chunk_lane_offset(b_voff, c);
 #pragma unroll
         for (int k = 0; k < kBInstr; ++k) {
           const int q = wave + C::kWaves * k;
-          dma16(rb, b_voff, static_cast<uint32_t>(8 * q * L + c * kChunk),
-                stage + C::kBOff + 8 * q * kChunk);
+          dma16(rb, bv + dma::rows_group(q, L, 0), stage + C::kBOff + 8 * q * kChunk);
         }
       }
       // scale rows: all 64 lanes (no divergence); lanes past the tile's rows read zeros
       if (wave == 0)
-        dma16(make_rsrc(sA + c * I + i0, imin64(I - i0, C::BM) * 4), 16 * lane, 0,
+        dma16(make_rsrc(sA + c * I + i0, imin64(I - i0, C::BM) * 4), 16 * lane,
               stage + C::kSAOff);
       if (C::kPerColScale && wave == (1 % C::kWaves))
-        dma16(make_rsrc(sB + c * J + j0, imin64(J - j0, C::BN) * 4), 16 * lane, 0,
+        dma16(make_rsrc(sB + c * J + j0, imin64(J - j0, C::BN) * 4), 16 * lane,
               stage + C::kSBOff);
     }
   }
@@ -264,18 +274,18 @@ struct Loader {
   // The share of issuing wave w (of kIssuers) in an 8-wave block: the A rows with the scale rows,
   // and the B rows.
   __device__ __forceinline__ void issue_as_a(lds_u8* stage, int64_t c, int w) const {
+    const uint32_t av = chunk_lane_offset(a_voff, c);
 #pragma unroll
     for (int k = 0; k < kAInstr; ++k) {
       const int q = w + kIssuers * k;
-      dma16(ra, a_voff, static_cast<uint32_t>(8 * q * L + c * kChunk),
-            stage + C::kAOff + 8 * q * kChunk);
+      dma16(ra, av + dma::rows_group(q, L, 0), stage + C::kAOff + 8 * q * kChunk);
     }
     // scale rows: all 64 lanes (no divergence); lanes past the tile's rows read zeros
     if (w == 0)
-      dma16(make_rsrc(sA + c * I + i0, imin64(I - i0, C::BM) * 4), 16 * lane, 0,
+      dma16(make_rsrc(sA + c * I + i0, imin64(I - i0, C::BM) * 4), 16 * lane,
             stage + C::kSAOff);
     if (C::kPerColScale && w == 1)
-      dma16(make_rsrc(sB + c * J + j0, imin64(J - j0, C::BN) * 4), 16 * lane, 0,
+      dma16(make_rsrc(sB + c * J + j0, imin64(J - j0, C::BN) * 4), 16 * lane,
             stage + C::kSBOff);
   }
   __device__ __forceinline__ void issue_as_b(lds_u8* stage, int64_t c, int w) const {
@@ -287,16 +297,14 @@ struct Loader {
 #pragma unroll
       for (int k = 0; k < kBInstr; ++k) {
         const int q = w + kIssuers * k;
-        const int sl = q >> 4, qq = q & 15;
-        dma16(rbc, bt_voff[k], static_cast<uint32_t>(8 * qq * J + 128 * sl),
-              stage + C::kBOff + 8 * q * kChunk);
+        dma16(rbc, bt_voff[k], stage + C::kBOff + 8 * q * kChunk);
       }
     } else {
+      const uint32_t bv = chunk_lane_offset(b_voff, c);
 #pragma unroll
       for (int k = 0; k < kBInstr; ++k) {
         const int q = w + kIssuers * k;
-        dma16(rb, b_voff, static_cast<uint32_t>(8 * q * L + c * kChunk),
-              stage + C::kBOff + 8 * q * kChunk);
+        dma16(rb, bv + dma::rows_group(q, L, 0), stage + C::kBOff + 8 * q * kChunk);
       }
     }
   }

@@ -64,16 +64,27 @@ def parse():
                    help="skip the optimizer-step measurement")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
+    p.add_argument("--config", choices=("c1", "c2", "c3", "all"), default=None,
+                   help="measure a single-layer configuration instead of the 28-layer step "
+                        "(c1: layer forward at M=4096; c2: layer fwd+bwd at M=16384; c3: down "
+                        "projection outlier stress; all: c1, c2, c3), one JSON line each")
+    p.add_argument("--no-copy-ceiling", action="store_true",
+                   help="skip the same-run copy ceiling and per-shape quantiser/copy rates")
     return p.parse_args()
 
 
 class Op:
-    """One launch of the step: its class, algorithmic flops / bytes, the call bound to the main
-    stream (serial order) and the call bound to its stream in the overlapped order, with the
-    events it waits for before launching and records after."""
+    """One launch of the step: its class (kind[shape]), the kernel function it runs,
+    algorithmic flops / bytes, the call bound to the main stream (serial order) and the call
+    bound to its stream in the overlapped order, with the events it waits for before launching
+    and records after."""
 
-    def __init__(self, cls, flops, nbytes, serial, par=None, side=False, waits=(), record=None):
+    def __init__(self, cls, flops, nbytes, serial, par=None, side=False, waits=(), record=None,
+                 fn=None, traffic=None):
         self.cls, self.flops, self.bytes = cls, flops, nbytes
+        self.fn = fn or cls.split("[")[0]  # the kernel function the launch runs
+        # the HBM bytes the launch must move at least (operands, scales and output once)
+        self.traffic = nbytes if traffic is None else traffic
         self.serial, self.par = serial, par or serial
         self.side, self.waits, self.record = side, tuple(waits), record
 
@@ -146,14 +157,25 @@ class Stack:
                        "dy": dy, "wq": wq, "sw": sw, "dw": dw}
                 self.linears.append(rec)
                 f = 2.0 * M * N * K
+                # least HBM bytes of each GEMM: e4m3 operands and fp32 scales read once, the
+                # output (bf16 Y / dX, fp32 dW) written once
+                t_fwd = M * K + 4 * M * K / 128 + N * K + 4 * N * K / 16384 + 2 * M * N
+                t_dgrad = M * N + 4 * M * N / 128 + N * K + 4 * N * K / 16384 + 2 * M * K
+                t_wgrad = N * M + 4 * N * M / 128 + K * M + 4 * K * M / 128 + 4 * N * K
                 group_w.append(w)
                 group_q.append(wq)
                 group_s.append(sw)
                 g_fwd = Op(f"gemm_fwd{sfx}[{name}]", f, 0.0,
                            *prep("puro_fp8_gemm_fwd", xq, sx, wq, sw, y, M, N, K),
-                           waits=(f"wq{layer}",) if li == 0 else ())
+                           waits=(f"wq{layer}",) if li == 0 else (),
+                           fn=B.puro_gemm_kernel_name("fwd", M, N, K, pow2), traffic=t_fwd)
                 g_dgrad = Op(f"gemm_dgrad{sfx}[{name}]", f, 0.0,
-                             *prep("puro_fp8_gemm_dgrad", dyq, sdy, wq, sw, dx, M, N, K))
+                             *prep("puro_fp8_gemm_dgrad", dyq, sdy, wq, sw, dx, M, N, K),
+                             fn=B.puro_gemm_kernel_name("dgrad", M, N, K, pow2),
+                             traffic=t_dgrad)
+                fn_wgrad = B.puro_gemm_kernel_name("wgrad", M, N, K, pow2)
+                qsfx = "[pow2]" if pow2 else ""
+                fn_dual = "quant_dual_1x128_kernel" + qsfx
                 # the gradient quantisation that overwrites slot li's transposed copy waits for
                 # the wgrad of the layer above (issued earlier) to have read it
                 reuse = (f"wg{li}",) if layer < layers - 1 else ()
@@ -163,48 +185,53 @@ class Stack:
                     sxt = torch.empty((M // 128, K), dtype=torch.float32, device=dev)
                     self.persist += [xtq, sxt]
                     rec.update(xtq=xtq, sxt=sxt)
-                    lf += [Op("quant_dual_1x128" + sfx, 0.0, M * K * B_DUAL,
-                              *prep("puro_quant_dual_1x128", x, M, K, xq, sx, xtq, sxt)),
+                    lf += [Op(f"quant_dual_1x128{sfx}[{M}x{K}]", 0.0, M * K * B_DUAL,
+                              *prep("puro_quant_dual_1x128", x, M, K, xq, sx, xtq, sxt),
+                              fn=fn_dual),
                            g_fwd]
                     bwd.append([
-                        Op("quant_dual_1x128" + sfx, 0.0, M * N * B_DUAL,
+                        Op(f"quant_dual_1x128{sfx}[{M}x{N}]", 0.0, M * N * B_DUAL,
                            *prep("puro_quant_dual_1x128", dy, M, N, dyq, sdy, dytq, sdyt),
-                           waits=reuse, record=f"dual{li}"),
+                           waits=reuse, record=f"dual{li}", fn=fn_dual),
                         g_dgrad,
                         Op(f"gemm_wgrad{sfx}[{name}]", f, 0.0,
                            *prep("puro_fp8_gemm_wgrad", dytq, sdyt, xtq, sxt, dw, M, N, K, 0,
                                  side=True),
-                           side=True, waits=(f"dual{li}",), record=f"wg{li}"),
+                           side=True, waits=(f"dual{li}",), record=f"wg{li}", fn=fn_wgrad,
+                           traffic=t_wgrad),
                     ])
                 else:
                     xtq = buf(("xtq", M, K), (K, M), torch.uint8)
                     sxt = buf(("sxt", M, K), (M // 128, K), torch.float32)
-                    lf += [Op("quant_act_1x128" + sfx, 0.0, M * K * B_ACT,
-                              *prep("puro_quant_act_1x128", x, M, K, xq, sx)),
+                    fn_act = "quant_act_1x128_kernel" + qsfx
+                    fn_tr = "quant_dual_1x128_kernel(columns only)" + qsfx
+                    lf += [Op(f"quant_act_1x128{sfx}[{M}x{K}]", 0.0, M * K * B_ACT,
+                              *prep("puro_quant_act_1x128", x, M, K, xq, sx), fn=fn_act),
                            g_fwd]
                     bwd.append([
-                        Op("quant_act_1x128" + sfx, 0.0, M * N * B_ACT,
-                           *prep("puro_quant_act_1x128", dy, M, N, dyq, sdy)),
+                        Op(f"quant_act_1x128{sfx}[{M}x{N}]", 0.0, M * N * B_ACT,
+                           *prep("puro_quant_act_1x128", dy, M, N, dyq, sdy), fn=fn_act),
                         g_dgrad,
                         # the transposed copies and wgrad only feed dW: all on the side stream,
                         # whose own order protects the buffers it reuses
-                        Op("quant_transpose" + sfx, 0.0, M * N * B_ACT,
+                        Op(f"quant_transpose{sfx}[{M}x{N}]", 0.0, M * N * B_ACT,
                            *prep("puro_quant_transpose", dy, M, N, dytq, sdyt, side=True),
-                           side=True),
-                        Op("quant_transpose" + sfx, 0.0, M * K * B_ACT,
+                           side=True, fn=fn_tr),
+                        Op(f"quant_transpose{sfx}[{M}x{K}]", 0.0, M * K * B_ACT,
                            *prep("puro_quant_transpose", x, M, K, xtq, sxt, side=True),
-                           side=True),
+                           side=True, fn=fn_tr),
                         Op(f"gemm_wgrad{sfx}[{name}]", f, 0.0,
                            *prep("puro_fp8_gemm_wgrad", dytq, sdyt, xtq, sxt, dw, M, N, K, 0,
                                  side=True),
-                           side=True),
+                           side=True, fn=fn_wgrad, traffic=t_wgrad),
                     ])
             # all four weights of the layer in one grouped launch
             items = B.w_group_items(group_w, group_q, group_s)
             wq_op = Op("quant_w_128x128" + sfx, 0.0,
                        sum(w.shape[0] * w.shape[1] for w in group_w) * B_W,
                        *prep("puro_quant_w_128x128_group", items, len(group_w), side=True),
-                       side=True, record=f"wq{layer}")
+                       side=True, record=f"wq{layer}",
+                       fn="quant_w_128x128_group_kernel" + ("[pow2]" if pow2 else ""))
             wq_ops.append(wq_op)
             fwd += [wq_op] + lf
         bwd_flat = [op for grp in reversed(bwd) for op in grp]
@@ -260,7 +287,7 @@ class Stack:
         self.graph.replay()
 
 
-def cpu_baseline(M: int, layers: int, rows_fwd: int = 64, rows_wgrad: int = 8,
+def cpu_baseline(M: int, layers: int, rows_fwd: int = 512, rows_wgrad: int = 512,
                  pow2: bool = False):
     """The oracle on the host cores, on a bounded sample of one step: every quantiser of one
     layer at full size, and each GEMM of that layer on a seeded sample of output rows (all
@@ -407,12 +434,14 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n}))
 
 
-def source_digest(kind: str) -> str:
-    """Digest of the kernel sources of a launch kind, to tell whether stored counters still
-    apply (GEMM kinds: gemm.hip; quantiser kinds: quant.hip; both with common.hpp)."""
+def source_digest(fn: str) -> str:
+    """Digest of the sources of a kernel function, to tell whether stored counters still apply
+    (GEMM functions: gemm.hip and its DMA offsets; quantiser functions: quant.hip; both with
+    common.hpp)."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("gemm.hip" if kind.startswith("gemm") else "quant.hip", "common.hpp"):
+    files = (("gemm.hip", "dma_offsets.hpp") if fn.startswith("gemm") else ("quant.hip",))
+    for f in files + ("common.hpp",):
         with open(os.path.join(ROOT, "blockwise_fp8_gemm_x128_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -421,20 +450,245 @@ def source_digest(kind: str) -> str:
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_qwen3_1p7b_linear_stack_M8192.txt")
 
 
-def stored_traffic(kind: str):
-    """Average HBM bytes per launch of a launch kind from the committed FETCH_SIZE / WRITE_SIZE
-    summary (its `traffic-record:` lines, counters already scaled by the copy-kernel factors),
-    or None if there is none or the kind's sources changed since the counters were taken."""
+def stored_traffic(fn: str):
+    """Average HBM bytes per launch of a kernel function in the step, from the committed
+    FETCH_SIZE / WRITE_SIZE summary (its `traffic-record:` lines, counters already scaled by the
+    copy-kernel factors), or None if there is none or the function's sources changed since the
+    counters were taken."""
     try:
         with open(TRAFFIC_SUMMARY) as fh:
             recs = [json.loads(l.split(":", 1)[1]) for l in fh if l.startswith("traffic-record:")]
     except (OSError, ValueError):
         return None
     for t in recs:
-        if t.get("kind") == kind and t.get("source_digest") == source_digest(kind):
+        if t.get("function") == fn and t.get("source_digest") == source_digest(fn):
             return 1024.0 * (t["fetch_kib_per_launch"] * t["fetch_factor"] +
                              t["write_kib_per_launch"] * t["write_factor"])
     return None
+
+
+def _loop_us(call, reps: int, stream) -> float:
+    """Average duration in us of `reps` back-to-back calls (call(i) launches rep i), from one
+    HIP event pair on the launch stream around the whole loop."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(2):
+        call(i)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(reps):
+        call(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return 1e3 * e0.elapsed_time(e1) / reps
+
+
+def copy_ceiling(reps: int = 10):
+    """Plain streaming ceiling measured in the same run: torch's elementwise negation of a
+    256 Mi-element bf16 tensor (512 MiB read, 512 MiB written, twice the 256 MB memory-side
+    cache), `reps` times back to back."""
+    import torch
+    st = torch.cuda.current_stream()
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    us = _loop_us(lambda i: torch.neg(src, out=dst), reps, st)
+    del src, dst
+    return {"gbps": 4.0 * n / (us * 1e-6) / 1e9, "bytes_per_call": 4 * n,
+            "kernel": "torch.neg on bf16 (2 B read + 2 B written per element)"}
+
+
+def quant_vs_copy(shapes, reps: int = 30, pow2: bool = False):
+    """Per quantiser shape of the step: the two-orientation quantiser and a plain copy of the
+    same bf16 input (torch.neg, 2 B read + 2 B written per element), each timed as `reps`
+    back-to-back launches rotating over enough input copies (> 1 GB) that the memory-side cache
+    cannot serve them; GB/s by each one's own bytes."""
+    import torch
+    from blockwise_fp8_gemm_x128_amd import binding as B
+    st = torch.cuda.current_stream()
+    out = {}
+    for rows, cols in shapes:
+        n = rows * cols
+        nc = max(2, -(-(1 << 30) // (2 * n)))
+        xs = [torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda").normal_()
+              for _ in range(nc)]
+        q = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+        qt = torch.empty((cols, rows), dtype=torch.uint8, device="cuda")
+        s = torch.empty((cols // 128, rows), dtype=torch.float32, device="cuda")
+        sT = torch.empty((rows // 128, cols), dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(xs[0])
+        name = "puro_quant_dual_1x128" + ("_pow2" if pow2 else "")
+        calls = [B.prepare(name, x, rows, cols, q, s, qt, sT, stream=st) for x in xs]
+        uq = _loop_us(lambda i: calls[i % nc](), reps, st)
+        uc = _loop_us(lambda i: torch.neg(xs[i % nc], out=dst), reps, st)
+        gq = n * B_DUAL / (uq * 1e-6) / 1e9
+        gc = 4.0 * n / (uc * 1e-6) / 1e9
+        out[f"{rows}x{cols}"] = {"quant_us": uq, "quant_gbps": gq, "copy_us": uc,
+                                 "copy_gbps": gc, "quant_over_copy": gq / gc}
+        del xs, calls, q, qt, s, sT, dst
+    return out
+
+
+# Single-layer configurations measured by `--config` (the default run is the 28-layer step):
+#   c1  one layer forward at M = 4096: quantise X per 1x128 group, W per 128x128 block, Y = X W^T
+#   c2  the same four linears, forward + data gradient + weight gradient at M = 16384, with the
+#       two-orientation quantiser for X and dY
+#   c3  the down projection's outlier stress inputs at M = 16384, forward + both gradients
+CONFIGS = {
+    "c1": {"M": 4096, "seed": 1, "linears": (0, 1, 2, 3), "backward": False,
+           "workload": "one Qwen3-1.7B-shaped layer forward (qkv, o, gate_up, down), M = 4096"},
+    "c2": {"M": 16384, "seed": 2, "linears": (0, 1, 2, 3), "backward": True,
+           "workload": "the four linears of one layer, fwd + dgrad + wgrad, M = 16384"},
+    "c3": {"M": 16384, "seed": 3, "linears": (3,), "backward": True, "outlier": True,
+           "workload": "down projection outlier stress (1% channels x100, 0.1% zero tiles, "
+                       "one 128x128 W block x50), fwd + dgrad + wgrad, M = 16384"},
+}
+
+
+def run_config(name: str, reps: int, cpu: bool):
+    """One JSON line for a single-layer configuration: every GEMM's TFLOP/s and every
+    quantiser's GB/s (each timed as `reps` back-to-back launches with one HIP event pair;
+    quantisers rotate over input copies totalling > 1 GB, GEMMs reuse one set of operands) with
+    their fractions of the 5.0 PFLOP/s and 8 TB/s peaks and the roofline times; and the oracle
+    on the host cores (full size for c1 and c3, 512 sampled output rows per GEMM for c2)."""
+    import numpy as np
+    import torch
+    from blockwise_fp8_gemm_x128_amd import binding as B
+    from blockwise_fp8_gemm_x128_amd import synth
+
+    cfg = CONFIGS[name]
+    M = cfg["M"]
+    st = torch.cuda.current_stream()
+    gemms, quants = {}, {}
+    host = []  # bf16 inputs per linear, for the oracle
+    for li in cfg["linears"]:
+        lname, K, N = synth.LINEARS[li]
+        if cfg.get("outlier"):
+            x, w, dy, _ = synth.outlier_inputs(M=M, K=K, N=N, config=cfg["seed"], linear=li)
+        else:
+            x, w, dy = synth.linear_inputs(cfg["seed"], li, M, K, N)
+        host.append((lname, K, N, x, w, dy))
+        nc = max(2, -(-(1 << 30) // (2 * M * max(K, N))))
+        xs = [x.cuda() for _ in range(nc)]
+        dys = [dy.cuda() for _ in range(nc)] if cfg["backward"] else []
+        wd = w.cuda()
+        f = 2.0 * M * N * K
+        wq, sw = B.puro_quant_w_128x128(wd)
+        P = B.prepare
+        c = P("puro_quant_w_128x128", wd, N, K, wq, sw, stream=st)
+        quants[f"quant_w_128x128[{lname} {N}x{K}]"] = {"us": _loop_us(lambda i: c(), reps, st),
+                                                       "bytes": N * K * B_W}
+        if not cfg["backward"]:
+            xq, sx = B.puro_quant_act_1x128(xs[0])
+            cs = [P("puro_quant_act_1x128", xx, M, K, xq, sx, stream=st) for xx in xs]
+            us = _loop_us(lambda i: cs[i % nc](), reps, st)
+            quants[f"quant_act_1x128[{lname} X {M}x{K}]"] = {"us": us, "bytes": M * K * B_ACT}
+            y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            c = P("puro_fp8_gemm_fwd", xq, sx, wq, sw, y, M, N, K, stream=st)
+            gemms[f"fwd[{lname}]"] = {"us": _loop_us(lambda i: c(), reps, st), "flops": f,
+                                      "kernel": B.puro_gemm_kernel_name("fwd", M, N, K)}
+            del xs
+            continue
+        xq, sx, xtq, sxt = B.puro_quant_dual_1x128(xs[0])
+        cs = [P("puro_quant_dual_1x128", xx, M, K, xq, sx, xtq, sxt, stream=st) for xx in xs]
+        us = _loop_us(lambda i: cs[i % nc](), reps, st)
+        quants[f"quant_dual_1x128[{lname} X {M}x{K}]"] = {"us": us, "bytes": M * K * B_DUAL}
+        dyq, sdy, dytq, sdyt = B.puro_quant_dual_1x128(dys[0])
+        cs = [P("puro_quant_dual_1x128", dd, M, N, dyq, sdy, dytq, sdyt, stream=st) for dd in dys]
+        us = _loop_us(lambda i: cs[i % nc](), reps, st)
+        quants[f"quant_dual_1x128[{lname} dY {M}x{N}]"] = {"us": us, "bytes": M * N * B_DUAL}
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device="cuda")
+        dw = torch.empty((N, K), dtype=torch.float32, device="cuda")
+        for op, c in (("fwd", P("puro_fp8_gemm_fwd", xq, sx, wq, sw, y, M, N, K, stream=st)),
+                      ("dgrad", P("puro_fp8_gemm_dgrad", dyq, sdy, wq, sw, dx, M, N, K,
+                                  stream=st)),
+                      ("wgrad", P("puro_fp8_gemm_wgrad", dytq, sdyt, xtq, sxt, dw, M, N, K, 0,
+                                  stream=st))):
+            gemms[f"{op}[{lname}]"] = {"us": _loop_us(lambda i: c(), reps, st), "flops": f,
+                                       "kernel": B.puro_gemm_kernel_name(op, M, N, K)}
+        del xs, dys
+    for d in gemms.values():
+        d["tflops"] = d["flops"] / (d["us"] * 1e-6) / 1e12
+        d["frac_fp8_peak"] = d["tflops"] / PEAK_FP8_TFLOPS
+        d["roofline_us"] = d["flops"] / (PEAK_FP8_TFLOPS * 1e12) * 1e6
+    for d in quants.values():
+        d["gbps"] = d["bytes"] / (d["us"] * 1e-6) / 1e9
+        d["frac_hbm_peak"] = d["gbps"] / PEAK_HBM_GBPS
+        d["roofline_us"] = d["bytes"] / (PEAK_HBM_GBPS * 1e9) * 1e6
+    g_us = sum(d["us"] for d in gemms.values())
+    q_us = sum(d["us"] for d in quants.values())
+    g_fl = sum(d["flops"] for d in gemms.values())
+    q_by = sum(d["bytes"] for d in quants.values())
+    out = {
+        "metric": METRIC,
+        "value": g_fl / (g_us * 1e-6) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": reps, "warmup": 2, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic (seeded N(0,1) X, N(0,0.02^2) W, N(0,1e-3^2) dY, bf16)",
+        "config": {"workload": cfg["workload"], "name": name, "tokens": M},
+        "gemm_tflops": g_fl / (g_us * 1e-6) / 1e12,
+        "gemm_frac_fp8_peak": g_fl / (g_us * 1e-6) / 1e12 / PEAK_FP8_TFLOPS,
+        "gemm_us": g_us, "gemm_roofline_us": g_fl / (PEAK_FP8_TFLOPS * 1e12) * 1e6,
+        "quant_gbps": q_by / (q_us * 1e-6) / 1e9,
+        "quant_frac_hbm_peak": q_by / (q_us * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+        "quant_us": q_us, "quant_roofline_us": q_by / (PEAK_HBM_GBPS * 1e9) * 1e6,
+        "gemms": gemms, "quantisers": quants,
+        "timing": ("HIP event pair around reps back-to-back launches on the launch stream; "
+                   "quantisers rotate over input copies totalling > 1 GB; GEMMs reuse one set "
+                   "of operands"),
+    }
+    if cpu:
+        out["cpu_baseline"] = config_cpu_baseline(name, host, M, cfg["backward"])
+    return out
+
+
+def config_cpu_baseline(name, host, M, backward):
+    """The oracle on the host cores for one configuration: every quantiser at full size; the
+    GEMMs at full size (c1, c3) or on 512 seeded sampled output rows each, extrapolated linearly
+    (c2)."""
+    import numpy as np
+
+    import oracle
+    rows_n = None if name in ("c1", "c3") else 512
+    rng = np.random.default_rng(0)
+    t_q = t_g = 0.0
+    flops = 0.0
+
+    def u16(t):
+        return t.contiguous().view(__import__("torch").int16).numpy().view(np.uint16)
+
+    for lname, K, N, x, w, dy in host:
+        t0 = time.perf_counter()
+        wq, sw = oracle.quant_w_128x128(u16(w))
+        xq, sx = oracle.quant_act_1x128(u16(x))
+        if backward:
+            dyq, sdy = oracle.quant_act_1x128(u16(dy))
+            dytq, sdyt = oracle.quant_transpose(u16(dy))
+            xtq, sxt = oracle.quant_transpose(u16(x))
+        t_q += time.perf_counter() - t0
+        rm = None if rows_n is None else np.sort(rng.choice(M, rows_n, replace=False))
+        rw = None if rows_n is None else np.sort(rng.choice(N, min(rows_n, N), replace=False))
+        sc_m = 1.0 if rm is None else M / len(rm)
+        sc_n = 1.0 if rw is None else N / len(rw)
+        t0 = time.perf_counter()
+        oracle.gemm_fwd(xq, sx, wq, sw, rows=rm)
+        t_g += (time.perf_counter() - t0) * sc_m
+        flops += 2.0 * M * N * K
+        if backward:
+            t0 = time.perf_counter()
+            oracle.gemm_dgrad(dyq, sdy, wq, sw, rows=rm)
+            t_g += (time.perf_counter() - t0) * sc_m
+            t0 = time.perf_counter()
+            oracle.gemm_wgrad(dytq, sdyt, xtq, sxt, rows=rw)
+            t_g += (time.perf_counter() - t0) * sc_n
+            flops += 4.0 * M * N * K
+    return {"value": flops / t_g / 1e9, "unit": "GFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "gemm_s": t_g, "quant_s": t_q,
+            "sample": ("every GEMM at full size" if rows_n is None else
+                       f"each GEMM on {rows_n} sampled output rows (all columns), extrapolated "
+                       f"linearly to all rows") + "; every quantiser at full size (timed apart)"}
 
 
 def main():
@@ -450,6 +704,11 @@ def main():
     import torch
 
     assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    if args.config:
+        for name in (("c1", "c2", "c3") if args.config == "all" else (args.config,)):
+            print(json.dumps(run_config(name, max(args.steps, 5), not args.no_cpu_baseline)),
+                  flush=True)
+        return
     M = M_TOKENS
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):  # every launch is bound to this stream when prepared
@@ -533,19 +792,50 @@ def main():
         else:
             e["gbps"] = by / secs / 1e9
             e["frac_hbm_peak"] = e["gbps"] / PEAK_HBM_GBPS
-    # Dominant kernel: the launch kind (one kernel function per kind; its launches differ only
-    # in shape) with the most time per step. achieved = its algorithmic work per launch,
-    # averaged over its launches, / its average launch duration.
+    # Per kernel function: the launches that run the same compiled kernel (one function can
+    # serve several shapes; one launch kind can use several functions).
+    by_fn = {}
+    for evs in ev_sets:
+        for op, (e0, e1) in zip(stack.launches, evs):
+            d = by_fn.setdefault(op.fn, {"ms": 0.0, "launches": 0, "flops": 0.0, "bytes": 0.0,
+                                         "traffic": 0.0, "classes": set()})
+            d["ms"] += e0.elapsed_time(e1)
+            d["launches"] += 1
+            d["flops"] += op.flops
+            d["bytes"] += op.bytes
+            d["traffic"] += op.traffic
+            d["classes"].add(op.cls)
+    kernels_by_fn = {}
+    for fn, d in by_fn.items():
+        secs = d["ms"] * 1e-3
+        ent = {"ms_per_step": d["ms"] / args.steps,
+               "launches_per_step": d["launches"] // args.steps,
+               "avg_launch_us": 1e3 * d["ms"] / d["launches"],
+               "work_per_launch": (d["flops"] or d["bytes"]) / d["launches"],
+               "traffic_bytes_per_launch": d["traffic"] / d["launches"],
+               "classes": sorted(d["classes"])}
+        if d["flops"]:
+            ent["tflops"] = d["flops"] / secs / 1e12
+            ent["frac_fp8_peak"] = ent["tflops"] / PEAK_FP8_TFLOPS
+        else:
+            ent["gbps"] = d["bytes"] / secs / 1e9
+            ent["frac_hbm_peak"] = ent["gbps"] / PEAK_HBM_GBPS
+        kernels_by_fn[fn] = ent
+    # Dominant kernel: the kernel function with the most time per step. achieved = its
+    # algorithmic work per launch, averaged over its launches (flops or bytes of all its
+    # launches / their number), / its average launch duration (HIP events on the launch stream).
     roofline = None
-    if by_kind:
-        dom = max(by_kind, key=lambda c: by_kind[c]["ms_per_step"])
-        k = by_kind[dom]
+    if kernels_by_fn:
+        dom = max(kernels_by_fn, key=lambda c: kernels_by_fn[c]["ms_per_step"])
+        k = kernels_by_fn[dom]
         common = {"traffic": stored_traffic(dom),
-                  "traffic_unit": "HBM bytes per launch, averaged over the kind's launches "
+                  "traffic_unit": "HBM bytes per launch, averaged over the function's launches "
                                   "(rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a plain copy "
                                   "kernel)",
                   "kernel": dom, "avg_launch_us": k["avg_launch_us"],
                   "launches_per_step": k["launches_per_step"],
+                  "work_per_launch": (by_fn[dom]["flops"] or by_fn[dom]["bytes"]) /
+                                     by_fn[dom]["launches"],
                   "source_digest": source_digest(dom)}
         if "tflops" in k:
             roofline = {"bound": "mfma", "achieved": k["tflops"], "peak": PEAK_FP8_TFLOPS,
@@ -597,6 +887,7 @@ def main():
                          if overlap else "serial, one stream"),
         "kernel_timing": "HIP event pair per launch, serial order on one stream",
         "kernel_timing_pass_ms_per_step": eager_ms_per_step,
+        "kernels_by_function": kernels_by_fn,
         "kernels_by_kind": by_kind,
         "kernels": kernels,
         "roofline": roofline,
@@ -604,6 +895,12 @@ def main():
     if not args.no_optim:
         with torch.cuda.stream(side):
             out["optimizer"] = optimizer_bench(stack, args.steps)
+    if not args.no_copy_ceiling:
+        del stack
+        torch.cuda.empty_cache()
+        out["copy_ceiling"] = copy_ceiling()
+        out["quant_vs_copy"] = quant_vs_copy(
+            sorted({(M, n) for n in (2048, 4096, 6144, 12288)}), pow2=args.pow2)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(M, args.layers, pow2=args.pow2)
     print(json.dumps(out), flush=True)

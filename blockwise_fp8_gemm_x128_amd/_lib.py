@@ -44,6 +44,7 @@ SIGNATURES = {
     "puro_fp8_gemm_dgrad": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P], ctypes.c_int),
     "puro_fp8_gemm_wgrad": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P],
                             ctypes.c_int),
+    "puro_gemm_kernel_name": ([ctypes.c_int, _I64, _I64, _I64, ctypes.c_int], ctypes.c_char_p),
 }
 SIGNATURES.update({
     "puro_frobenius_norm": ([_P, _I64, _P, _P, _P], ctypes.c_int),

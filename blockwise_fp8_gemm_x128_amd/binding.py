@@ -254,6 +254,14 @@ puro_fp8_gemm_dgrad_pow2 = _pow2_variant(puro_fp8_gemm_dgrad)
 puro_fp8_gemm_wgrad_pow2 = _pow2_variant(puro_fp8_gemm_wgrad)
 
 
+def puro_gemm_kernel_name(op: str, M: int, N: int, K: int, pow2: bool = False) -> str:
+    """Name of the kernel function puro_fp8_gemm_<op> (op: 'fwd', 'dgrad' or 'wgrad') launches
+    for these sizes on the current device, or '' if it would launch nothing."""
+    code = {"fwd": 0, "dgrad": 1, "wgrad": 2}[op]
+    res = lib().puro_gemm_kernel_name(code, M, N, K, int(bool(pow2)))
+    return res.decode() if res else ""
+
+
 def prepare(name: str, *args, stream=None):
     """Pre-marshalled call of a C entry point for hot loops: tensors become raw device
     pointers, `stream` (a torch.cuda.Stream; default the current torch stream) is bound, and the

@@ -1156,3 +1156,33 @@ extern "C" puro_status puro_fp8_gemm_wgrad_pow2(const void* dytq, const float* s
                                                 void* stream) {
   return gemm_wgrad<true>(dytq, sdyt, xtq, sxt, dw, M, N, K, accumulate, stream);
 }
+
+// Name of the kernel function a GEMM entry point launches for the given sizes, from the same
+// shape choice the entry point makes (for profiling and per-kernel accounting).
+extern "C" const char* puro_gemm_kernel_name(int op, int64_t M, int64_t N, int64_t K, int pow2) {
+  if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K) || (pow2 != 0 && pow2 != 1)) return nullptr;
+  static const char* const kFwd[2][2] = {{"gemm_fwd_128x128", "gemm_fwd_256x256"},
+                                         {"gemm_fwd_128x128_pow2", "gemm_fwd_256x256_pow2"}};
+  static const char* const kDgrad[2][2] = {
+      {"gemm_dgrad_128x128", "gemm_dgrad_256x256"},
+      {"gemm_dgrad_128x128_pow2", "gemm_dgrad_256x256_pow2"}};
+  switch (op) {
+    case 0:
+      if (M == 0 || N == 0) return nullptr;
+      return kFwd[pow2][use_big_tiles(M, N) ? 1 : 0];
+    case 1:
+      if (M == 0 || K == 0) return nullptr;
+      return kDgrad[pow2][use_big_tiles(M, K) ? 1 : 0];
+    case 2: {
+      if (N == 0 || K == 0) return nullptr;
+      static const char* const kWgrad[2][5] = {
+          {"gemm_wgrad_256x256", "gemm_wgrad_128x128", "gemm_wgrad_256x192",
+           "gemm_wgrad_192x256", "gemm_wgrad_128x128_k2"},
+          {"gemm_wgrad_256x256_pow2", "gemm_wgrad_128x128_pow2", "gemm_wgrad_256x192_pow2",
+           "gemm_wgrad_192x256_pow2", "gemm_wgrad_128x128_k2_pow2"}};
+      return kWgrad[pow2][pick_wgrad_shape(N, K)];
+    }
+    default:
+      return nullptr;
+  }
+}

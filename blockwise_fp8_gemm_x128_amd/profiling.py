@@ -1,0 +1,193 @@
+"""Text summaries of rocprofv3 output from bench.py runs, per kernel function of the library.
+
+    python -m blockwise_fp8_gemm_x128_amd.profiling time STATS_CSV BENCH_LOG [--title T]
+        kernel time per function (rocprofv3 --kernel-trace --stats) beside the algorithmic
+        work per launch and the HIP-event durations that the same profiled bench run printed
+    python -m blockwise_fp8_gemm_x128_amd.profiling traffic FETCH_CSV WRITE_CSV CFETCH_CSV CWRITE_CSV
+        HBM bytes per launch per function from two counter passes (FETCH_SIZE, then
+        WRITE_SIZE, KiB per dispatch), each scaled by the same counter's reading for a plain
+        copy of known size (bench.py --copy-calibration), with one `traffic-record:` line per
+        function that bench.py reads back while the function's sources are unchanged
+
+Kernel names are reduced to the names bench.py accounts launches under (the function name,
+with "(columns only)" for the transposed quantiser's instance of the two-orientation kernel and
+"[pow2]" for power-of-two-scale instances of templated kernels).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import json
+import os
+import re
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def function_of(kernel_name: str) -> str:
+    """Library function name of a rocprofv3 kernel name ('' for kernels of other libraries)."""
+    m = re.search(r"puro::\(anonymous namespace\)::([A-Za-z0-9_]+)(<([^>]*)>)?\(", kernel_name)
+    if not m:
+        return ""
+    name, targs = m.group(1), (m.group(3) or "")
+    args = [a.strip() for a in targs.split(",")] if targs else []
+    if name.startswith("quant_") and args:
+        pow2 = args[0] == "true"
+        if name == "quant_dual_1x128_kernel" and len(args) > 1 and args[1] == "false":
+            name += "(columns only)"
+        return name + ("[pow2]" if pow2 else "")
+    if args:
+        return f"{name}<{', '.join(args)}>"
+    return name
+
+
+def _rows(path):
+    with open(path, newline="") as fh:
+        return list(csv.DictReader(fh))
+
+
+def bench_json(log_path: str):
+    """The JSON line bench.py printed (last line of the log that parses as a JSON object)."""
+    out = None
+    with open(log_path) as fh:
+        for line in fh:
+            line = line.strip()
+            if line.startswith("{") and line.endswith("}"):
+                try:
+                    out = json.loads(line)
+                except ValueError:
+                    pass
+    return out
+
+
+def time_summary(stats_csv: str, log_path: str, title: str) -> str:
+    rows = _rows(stats_csv)
+    b = bench_json(log_path) or {}
+    fns = b.get("kernels_by_function", {})
+    total_ns = sum(float(r["TotalDurationNs"]) for r in rows)
+    lines = [title, "",
+             "rocprofv3 --stats, this library's kernels (the run's other kernels are torch's input",
+             "generation and the copy/calibration helpers):",
+             f"  {'function':38s} {'calls':>6s} {'total ms':>9s} {'avg us':>8s} {'min us':>8s} "
+             f"{'max us':>8s} {'% time':>7s} {'events us':>9s} {'rate (rocprof avg)':>20s}"]
+    per = []
+    for r in rows:
+        fn = function_of(r["Name"])
+        if not fn:
+            continue
+        avg_us = float(r["AverageNs"]) / 1e3
+        ent = fns.get(fn, {})
+        work = ent.get("work_per_launch")
+        rate = ""
+        if work:
+            if fn.startswith("gemm"):
+                rate = f"{work / (avg_us * 1e-6) / 1e12:9.1f} TFLOP/s ({work / (avg_us * 1e-6) / 5e15:.3f})"
+            else:
+                rate = f"{work / (avg_us * 1e-6) / 1e9:9.1f} GB/s ({work / (avg_us * 1e-6) / 8e12:.3f})"
+        ev = ent.get("avg_launch_us")
+        per.append(float(r["TotalDurationNs"]))
+        lines.append(f"  {fn:38s} {int(r['Calls']):6d} {float(r['TotalDurationNs']) / 1e6:9.3f} "
+                     f"{avg_us:8.2f} {float(r['MinNs']) / 1e3:8.2f} {float(r['MaxNs']) / 1e3:8.2f} "
+                     f"{100.0 * float(r['TotalDurationNs']) / total_ns:7.2f} "
+                     f"{(f'{ev:9.2f}' if ev else ' ' * 9)} {rate:>20s}")
+    lines += ["",
+              "'events us' is the same function's average HIP-event duration in the bench's",
+              "kernel timing pass of this run; the rate is the algorithmic work per launch",
+              "(flops or bytes, averaged over the function's launches in the step) over the",
+              "rocprof average, with its fraction of 5.0 PFLOP/s or 8 TB/s in parentheses."]
+    if b:
+        lines += ["", f"bench line of the profiled run: {b.get('ms_per_step', 0):.2f} ms per step, "
+                      f"{b.get('value', 0):.0f} tokens/s (dominant function "
+                      f"{b.get('roofline', {}).get('kernel')}, frac "
+                      f"{b.get('roofline', {}).get('frac', 0):.3f} by events)"]
+    return "\n".join(lines) + "\n"
+
+
+def _counter_per_fn(path: str):
+    acc = {}
+    for r in _rows(path):
+        fn = function_of(r["Kernel_Name"])
+        if not fn:
+            continue
+        d = acc.setdefault(fn, [0.0, 0])
+        d[0] += float(r["Counter_Value"])
+        d[1] += 1
+    return {fn: v / n for fn, (v, n) in acc.items()}
+
+
+def _copy_kib(path: str) -> float:
+    """Counter reading of the calibration copy (the largest neg kernel dispatch)."""
+    best = 0.0
+    for r in _rows(path):
+        if "neg_kernel" in r["Kernel_Name"]:
+            best = max(best, float(r["Counter_Value"]))
+    if best <= 0:
+        raise SystemExit(f"{path}: no calibration copy dispatch found")
+    return best
+
+
+def traffic_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv, title: str,
+                    algorithmic=None) -> str:
+    sys.path.insert(0, ROOT)
+    import bench  # the source digests bench.py checks the records against
+
+    copy_bytes = 1 << 30  # bench.py --copy-calibration: 2^28 fp32 read and written once
+    ff = copy_bytes / (_copy_kib(cfetch_csv) * 1024.0)
+    wf = copy_bytes / (_copy_kib(cwrite_csv) * 1024.0)
+    fetch, write = _counter_per_fn(fetch_csv), _counter_per_fn(write_csv)
+    lines = [title, "",
+             f"Calibration (plain copy, 1 GiB read and 1 GiB written): fetch factor {ff:.5f}, "
+             f"write factor {wf:.5f}",
+             "(HBM bytes = FETCH_SIZE KiB x 1024 x fetch factor + WRITE_SIZE KiB x 1024 x write "
+             "factor)", "",
+             f"  {'function':38s} {'read MB':>9s} {'write MB':>9s} {'total MB':>9s} "
+             f"{'algorithmic':>11s} {'ratio':>6s}"]
+    recs = []
+    for fn in sorted(set(fetch) & set(write)):
+        rd = fetch[fn] * 1024.0 * ff / 1e6
+        wr = write[fn] * 1024.0 * wf / 1e6
+        alg = (algorithmic or {}).get(fn)
+        lines.append(f"  {fn:38s} {rd:9.2f} {wr:9.2f} {rd + wr:9.2f} "
+                     f"{(f'{alg / 1e6:11.2f}' if alg else ' ' * 11)} "
+                     f"{(f'{(rd + wr) * 1e6 / alg:6.2f}' if alg else '')}")
+        if fn.startswith(("gemm", "quant")):
+            recs.append({"function": fn, "fetch_kib_per_launch": fetch[fn],
+                         "write_kib_per_launch": write[fn], "fetch_factor": ff,
+                         "write_factor": wf, "source_digest": bench.source_digest(fn)})
+    lines += ["", "Records read by bench.py (counters averaged over the function's launches; "
+                  "valid while its sources hash to source_digest):"]
+    lines += ["traffic-record: " + json.dumps(r) for r in recs]
+    return "\n".join(lines) + "\n"
+
+
+def main(argv=None):
+    p = argparse.ArgumentParser()
+    sub = p.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("time")
+    t.add_argument("stats_csv")
+    t.add_argument("bench_log")
+    t.add_argument("--title", default="Kernel time per function")
+    r = sub.add_parser("traffic")
+    r.add_argument("fetch_csv")
+    r.add_argument("write_csv")
+    r.add_argument("cfetch_csv")
+    r.add_argument("cwrite_csv")
+    r.add_argument("--bench-log", default=None,
+                   help="bench.py output of the counter run, for the algorithmic bytes")
+    r.add_argument("--title", default="HBM traffic per launch per function")
+    a = p.parse_args(argv)
+    if a.cmd == "time":
+        sys.stdout.write(time_summary(a.stats_csv, a.bench_log, a.title))
+    else:
+        alg = None
+        if a.bench_log:
+            b = bench_json(a.bench_log) or {}
+            alg = {fn: e.get("traffic_bytes_per_launch")
+                   for fn, e in b.get("kernels_by_function", {}).items()}
+        sys.stdout.write(traffic_summary(a.fetch_csv, a.write_csv, a.cfetch_csv, a.cwrite_csv,
+                                         a.title, alg))
+
+
+if __name__ == "__main__":
+    main()

@@ -141,6 +141,13 @@ puro_status puro_fp8_gemm_wgrad(const void* dytq, const float* sdyt, const void*
                                 const float* sxt, float* dw, int64_t M, int64_t N, int64_t K,
                                 int accumulate, void* stream);
 
+/* Name of the kernel function puro_fp8_gemm_fwd (op 0), _dgrad (op 1) or _wgrad (op 2) -- or
+ * its _pow2 twin when pow2 = 1 -- launches for the given sizes (e.g. "gemm_fwd_256x256"), as
+ * the entry point itself chooses it on the current device; NULL when the call would launch
+ * nothing or its arguments are invalid. For profiling and per-kernel accounting; static
+ * storage, host only, enqueues nothing. */
+const char* puro_gemm_kernel_name(int op, int64_t M, int64_t N, int64_t K, int pow2);
+
 /* ---------------------------------------------------------------- optimizer step
  * PuRo-2B news post (jj-blog-4lo.pages.dev), optimizer paragraph after the training-recipe
  * paragraph: the roughly scale-invariant matrices (the linear-layer weights) are updated and

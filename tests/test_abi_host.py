@@ -167,3 +167,23 @@ def test_optim_validation(L):
                 PuroAdamWParams(float("inf"), 0.9, 0.95, 1e-8, 0.1, 1)):
         assert adamw(FAKE, FAKE, FAKE, FAKE, 8, ctypes.byref(bad), None, None) == 5
     assert adamw(None, None, None, None, 0, ctypes.byref(ok), None, None) == 0
+
+
+def test_gemm_kernel_names(L):
+    # the kernel each GEMM entry point picks for the Qwen3-1.7B-shaped layer at M = 8192 on a
+    # 256-CU part (no device here: the shape picker assumes 256 compute units)
+    name = lambda op, M, N, K, p=0: (L.puro_gemm_kernel_name(op, M, N, K, p) or b"").decode()  # noqa: E731
+    for K, N in ((2048, 4096), (2048, 2048), (2048, 12288), (6144, 2048)):
+        assert name(0, 8192, N, K) == "gemm_fwd_256x256"
+        assert name(1, 8192, N, K) == "gemm_dgrad_256x256"
+        assert name(0, 8192, N, K, 1) == "gemm_fwd_256x256_pow2"
+    assert name(2, 8192, 4096, 2048) == "gemm_wgrad_128x128"
+    assert name(2, 8192, 2048, 2048) == "gemm_wgrad_128x128_k2"
+    assert name(2, 8192, 12288, 2048) == "gemm_wgrad_192x256"
+    assert name(2, 8192, 2048, 6144) == "gemm_wgrad_256x192"
+    assert name(2, 8192, 4096, 4096) == "gemm_wgrad_256x256"
+    assert name(0, 256, 256, 256) == "gemm_fwd_128x128"
+    assert name(1, 256, 256, 256, 1) == "gemm_dgrad_128x128_pow2"
+    assert name(0, 0, 256, 256) == "" and name(0, 130, 256, 256) == "" and name(3, 128, 128, 128) == ""
+    assert name(0, 128, 128, 128, 2) == ""
+

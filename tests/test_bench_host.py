@@ -19,10 +19,11 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in r.stderr
 
 
-def test_source_digest_depends_on_the_kind():
-    g, q = bench.source_digest("gemm_fwd"), bench.source_digest("quant_dual_1x128")
+def test_source_digest_depends_on_the_function():
+    g = bench.source_digest("gemm_fwd_256x256")
+    q = bench.source_digest("quant_dual_1x128_kernel")
     assert len(g) == len(q) == 16 and g != q
-    assert bench.source_digest("gemm_wgrad") == g
+    assert bench.source_digest("gemm_wgrad_192x256") == g
 
 
 def _write_summary(path, recs):
@@ -35,15 +36,16 @@ def _write_summary(path, recs):
 def test_stored_traffic_uses_only_matching_records(tmp_path, monkeypatch):
     path = tmp_path / "traffic.txt"
     monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", str(path))
-    good = {"kind": "gemm_fwd", "fetch_kib_per_launch": 100.0, "write_kib_per_launch": 50.0,
-            "fetch_factor": 2.0, "write_factor": 1.0, "source_digest": bench.source_digest("gemm_fwd")}
-    stale = dict(good, kind="gemm_dgrad", source_digest="0" * 16)
+    fwd = "gemm_fwd_256x256"
+    good = {"function": fwd, "fetch_kib_per_launch": 100.0, "write_kib_per_launch": 50.0,
+            "fetch_factor": 2.0, "write_factor": 1.0, "source_digest": bench.source_digest(fwd)}
+    stale = dict(good, function="gemm_dgrad_256x256", source_digest="0" * 16)
     _write_summary(path, [good, stale])
-    assert bench.stored_traffic("gemm_fwd") == 1024.0 * (100.0 * 2.0 + 50.0 * 1.0)
-    assert bench.stored_traffic("gemm_dgrad") is None    # sources changed since measured
-    assert bench.stored_traffic("quant_dual_1x128") is None  # no record
+    assert bench.stored_traffic(fwd) == 1024.0 * (100.0 * 2.0 + 50.0 * 1.0)
+    assert bench.stored_traffic("gemm_dgrad_256x256") is None  # sources changed since measured
+    assert bench.stored_traffic("quant_dual_1x128_kernel") is None  # no record
     monkeypatch.setattr(bench, "TRAFFIC_SUMMARY", str(tmp_path / "missing.txt"))
-    assert bench.stored_traffic("gemm_fwd") is None
+    assert bench.stored_traffic(fwd) is None
 
 
 def test_committed_summary_parses():
@@ -52,7 +54,8 @@ def test_committed_summary_parses():
         for line in fh:
             if line.startswith("traffic-record:"):
                 recs.append(json.loads(line.split(":", 1)[1]))
-    kinds = {r["kind"] for r in recs}
-    assert {"gemm_fwd", "gemm_dgrad", "gemm_wgrad", "quant_dual_1x128", "quant_w_128x128"} <= kinds
+    fns = {r["function"] for r in recs}
+    assert {"gemm_fwd_256x256", "gemm_dgrad_256x256", "quant_dual_1x128_kernel",
+            "quant_w_128x128_group_kernel"} <= fns
     for r in recs:
         assert r["fetch_kib_per_launch"] > 0 and r["write_kib_per_launch"] > 0

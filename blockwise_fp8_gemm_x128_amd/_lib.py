@@ -49,6 +49,7 @@ SIGNATURES = {
 SIGNATURES.update({
     "puro_frobenius_norm": ([_P, _I64, _P, _P, _P], ctypes.c_int),
     "puro_hyperball_step": ([_P, _P, _I64, ctypes.c_float, _P, _P, _P, _P], ctypes.c_int),
+    "puro_hyperball_step_noalloc": ([_P, _P, _I64, ctypes.c_float, _P, _P, _P], ctypes.c_int),
     "puro_adamw_step": ([_P, _P, _P, _P, _I64, ctypes.POINTER(PuroAdamWParams), _P, _P],
                         ctypes.c_int),
 })

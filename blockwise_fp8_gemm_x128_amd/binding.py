@@ -210,6 +210,20 @@ def puro_hyperball_step(w: torch.Tensor, u: torch.Tensor, lr: float, radius: tor
     return w_bf16
 
 
+def puro_hyperball_step_noalloc(w: torch.Tensor, u: torch.Tensor, lr: float,
+                                radius: torch.Tensor, w_bf16: torch.Tensor):
+    """puro_hyperball_step with the library's own scratch instead of a workspace; the bf16
+    output is required (this path allocates nothing)."""
+    dev = _dev(w)
+    _need(w, "w", torch.float32, tuple(w.shape), dev)
+    _need(u, "u", torch.float32, tuple(w.shape), dev)
+    _need(radius, "radius", torch.float32, (1,), dev)
+    _need(w_bf16, "w_bf16", torch.bfloat16, tuple(w.shape), dev)
+    check(lib().puro_hyperball_step_noalloc(w.data_ptr(), u.data_ptr(), w.numel(), float(lr),
+                                            radius.data_ptr(), w_bf16.data_ptr(), _stream(dev)))
+    return w_bf16
+
+
 def adamw_params(lr, beta1, beta2, eps, weight_decay, step) -> PuroAdamWParams:
     return PuroAdamWParams(lr, beta1, beta2, eps, weight_decay, int(step))
 

@@ -14,6 +14,8 @@
 // reproducible run to run and device to device.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.hpp"
 
 namespace puro {
@@ -180,6 +182,31 @@ inline int stream_blocks(int64_t n4) {
 
 inline bool numel_ok(int64_t n) { return n >= 0 && n % 4 == 0 && n <= (int64_t(1) << 40); }
 
+// Scratch of the allocation-free projected step: the same partial sums the workspace argument
+// holds, in a device array of the library's own. Its size does not depend on the element count
+// (the reduction grid is capped at kOptMaxBlocks), so every valid call fits. Each device holds
+// its own copy; host code uses the address hipGetSymbolAddress reports for the current device,
+// never the array's name.
+static __device__ __align__(256) uint8_t scratch[PURO_OPT_WORKSPACE_BYTES];
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device, looked up once per device.
+puro_status scratch_ptr(void** out) {
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PURO_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return PURO_ERR_LAUNCH;
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return PURO_OK;
+}
+
 }  // namespace
 }  // namespace puro
 
@@ -223,6 +250,24 @@ extern "C" puro_status puro_hyperball_step(float* w, const float* u, int64_t num
   hipLaunchKernelGGL(scale_kernel, dim3(blocks), dim3(kOptThreads), 0, s, w, n4, partials, blocks,
                      radius, static_cast<uint16_t*>(w_bf16));
   return launch_status();
+}
+
+extern "C" puro_status puro_hyperball_step_noalloc(float* w, const float* u, int64_t numel,
+                                                   float lr, const float* radius, void* w_bf16,
+                                                   void* stream) {
+  // the same validation as puro_hyperball_step, before anything touches the device
+  if (!numel_ok(numel)) return PURO_ERR_SHAPE;
+  if (!isfinite(lr)) return PURO_ERR_ARG;
+  const bool empty = numel == 0;
+  PURO_TRY(check_ptr(w, empty));
+  PURO_TRY(check_ptr(u, empty));
+  PURO_TRY(check_ptr(w_bf16, empty));
+  if (empty) return PURO_OK;
+  if (radius == nullptr) return PURO_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(radius) & 3u) return PURO_ERR_ALIGN;
+  void* ws = nullptr;
+  PURO_TRY(scratch_ptr(&ws));
+  return puro_hyperball_step(w, u, numel, lr, radius, w_bf16, ws, stream);
 }
 
 extern "C" puro_status puro_adamw_step(float* p, const float* g, float* m, float* v,

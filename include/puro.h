@@ -181,6 +181,19 @@ puro_status puro_hyperball_step(float* w, const float* u, int64_t numel, float l
                                 const float* radius, void* w_bf16, void* workspace,
                                 void* stream);
 
+/* puro_hyperball_step without the workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the partial sums go to a scratch array the library keeps in device memory,
+ * PURO_OPT_WORKSPACE_BYTES per device, held until the process ends. Its need does not depend on
+ * numel, so every numel that puro_hyperball_step accepts fits (larger numel: PURO_ERR_SHAPE).
+ * Same arguments otherwise, same validation, same kernels and the same results bit for bit.
+ * The call allocates and frees nothing. The first call on a device looks up the array's
+ * address there (PURO_ERR_LAUNCH if that fails). All calls on one device share the array:
+ * calls that overlap in time on one device (different streams, no ordering between them) race
+ * and give wrong results; order them on one stream. */
+puro_status puro_hyperball_step_noalloc(float* w, const float* u, int64_t numel, float lr,
+                                        const float* radius, void* w_bf16, void* stream);
+
 /* AdamW with decoupled weight decay (Loshchilov and Hutter), in place on fp32 state:
  *   m = b1*m + (1-b1)*g;  v = b2*v + (1-b2)*g^2
  *   p = p*(1 - lr*wd) - lr * (m/(1-b1^t)) / (sqrt(v/(1-b2^t)) + eps)

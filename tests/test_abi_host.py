@@ -187,3 +187,14 @@ def test_gemm_kernel_names(L):
     assert name(0, 0, 256, 256) == "" and name(0, 130, 256, 256) == "" and name(3, 128, 128, 128) == ""
     assert name(0, 128, 128, 128, 2) == ""
 
+
+def test_noalloc_validation(L):
+    # invalid arguments are rejected before the device is touched
+    f = L.puro_hyperball_step_noalloc
+    assert f(FAKE, FAKE, 6, 0.1, FAKE, FAKE, None) == 2           # numel not a multiple of 4
+    assert f(FAKE, FAKE, (1 << 40) + 4, 0.1, FAKE, FAKE, None) == 2   # beyond the size limit
+    assert f(FAKE, None, 8, 0.1, FAKE, FAKE, None) == 1           # NULL direction
+    assert f(FAKE, FAKE, 8, 0.1, None, FAKE, None) == 1           # NULL radius
+    assert f(FAKE, FAKE, 8, 0.1, FAKE, MIS, None) == 3            # misaligned bf16 output
+    assert f(FAKE, FAKE, 8, float("inf"), FAKE, FAKE, None) == 5  # non-finite learning rate
+    assert f(None, None, 0, 0.1, None, None, None) == 0           # empty: nothing to do

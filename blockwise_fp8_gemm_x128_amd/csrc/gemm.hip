@@ -187,6 +187,7 @@ struct Loader {
   int wave, lane;
   const float* sb_block;  // block modes: the wave's block scale of chunk 0 (uniform)
   int64_t sb_block_step;
+  rsrc_t rsb;             // block modes: resource over the wave's block scales of every chunk
 
   __device__ __forceinline__ void init(int wn) {
     static_assert(kIssuers % 2 == 0, "row-major DMA swizzle assumes an even issuer count");
@@ -216,6 +217,19 @@ struct Loader {
       sb_block = sB + jb;
       sb_block_step = J / 128;
     }
+    const int64_t nk = L / kChunk;
+    rsb = make_rsrc(sb_block, nk > 0 ? ((nk - 1) * sb_block_step + 1) * 4 : 0);
+  }
+
+  // Block scale of chunk c (block modes), read with a vector load: a scalar load would share
+  // the counter of the LDS fragment reads and, since scalar loads may return out of order, make
+  // every wait on those reads a wait for all of them (measured: each chunk's first products
+  // waited for the whole chunk's fragments). The value is used one chunk later, after the
+  // barrier's wait for all vector memory.
+  __device__ __forceinline__ float block_scale(int64_t c) const {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(
+                   rsb, static_cast<int>(c * sb_block_step * 4), 0, 0));
   }
 
   // Enqueue chunk c into `stage` (the DMA writes LDS directly). A 4-wave block issues all of it
@@ -449,6 +463,9 @@ __device__ __forceinline__ void chunk_step(const lds_u8* stage, const FragOffset
   }
 }
 
+// The chunk's B fragments, issued in column order, each fence keeping that order: LDS reads
+// return in order, so the first product waits only for the first A and B fragments, not for
+// the whole chunk's reads.
 template <class C, int nj>
 __device__ __forceinline__ void load_bf(const lds_u8* stage, const FragOffsets<C>& o,
                                         ChunkState<C>& st, float sb_blk) {
@@ -458,19 +475,22 @@ __device__ __forceinline__ void load_bf(const lds_u8* stage, const FragOffsets<C
       st.sbv[nj] = *reinterpret_cast<const lds_v4f*>(stage + o.sb + 64 * nj);
     else
       st.sbv[nj] = sb_blk;
+    __builtin_amdgcn_sched_barrier(0);
     load_bf<C, nj + 1>(stage, o, st, sb_blk);
   }
 }
 
-// One 128-wide reduction chunk out of a landed stage.
+// One 128-wide reduction chunk out of a landed stage: the first A fragment is read first, then
+// the B fragments in the order the first row block multiplies them.
 template <class C, class Mid = NoMid>
 __device__ __forceinline__ void compute_chunk(const lds_u8* stage, float sb_blk,
                                               const FragOffsets<C>& o,
                                               v4f (&acc)[C::MI][C::NJ], const Mid& mid = Mid()) {
   ChunkState<C> st;
-  load_bf<C, 0>(stage, o, st, sb_blk);
   st.af_cur = frag_a<C, 0>(stage, o);
   st.sa_cur = scale_a<C, 0>(stage, o);
+  __builtin_amdgcn_sched_barrier(0);
+  load_bf<C, 0>(stage, o, st, sb_blk);
   chunk_step<C, 0>(stage, o, st, sb_blk, acc, mid);
 }
 
@@ -503,6 +523,7 @@ __device__ __forceinline__ void load_bf_pow2(const lds_u8* stage, const FragOffs
       st.eb[nj] = e8m0(*reinterpret_cast<const lds_f32*>(stage + o.sbr + 64 * nj));
     else
       st.eb[nj] = eb_blk;
+    __builtin_amdgcn_sched_barrier(0);
     load_bf_pow2<C, nj + 1>(stage, o, st, eb_blk);
   }
 }
@@ -537,9 +558,10 @@ __device__ __forceinline__ void compute_chunk_pow2(const lds_u8* stage, float sb
                                                    v4f (&acc)[C::MI][C::NJ],
                                                    const Mid& mid = Mid()) {
   Pow2State<C> st;
-  load_bf_pow2<C, 0>(stage, o, st, e8m0(sb_blk));
   st.af_cur = frag_a<C, 0>(stage, o);
   st.ea_cur = e8m0(scale_a<C, 0>(stage, o));
+  __builtin_amdgcn_sched_barrier(0);
+  load_bf_pow2<C, 0>(stage, o, st, e8m0(sb_blk));
   pow2_step<C, 0>(stage, o, st, acc, mid);
   // Pin the accumulators at the end of the chunk: without this, IR-level sinking moves the
   // chunk's instructions past the next barrier, keeping all its fragments live (spills).
@@ -734,7 +756,7 @@ __device__ __forceinline__ void gemm_body(const uint8_t* __restrict__ A,
     __syncthreads();
     if (c + 1 < nk) {
       ld.issue(nxt, c + 1);
-      if (!C::kPerColScale) sb_next = ld.sb_block[(c + 1) * ld.sb_block_step];
+      if (!C::kPerColScale) sb_next = ld.block_scale(c + 1);
     }
     auto mid = [&]() {  // runs before the chunk's second row block
       if (c + 1 < nk) ld.issue_second(nxt, c + 1);

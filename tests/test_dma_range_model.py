@@ -17,7 +17,10 @@ def test_dma_offsets_stay_in_range(tmp_path):
     if cxx is None:
         pytest.skip("no host C++ compiler")
     exe = str(tmp_path / "dma_range_model")
-    subprocess.check_call([cxx, "-std=c++17", "-O1", "-Wall", "-I" + CSRC,
+    # built with AddressSanitizer and UndefinedBehaviorSanitizer: the model's own arithmetic
+    # (offsets in 32 bits, products of tile sizes and pitches) must not overflow
+    subprocess.check_call([cxx, "-std=c++17", "-O1", "-Wall", "-fsanitize=address,undefined",
+                           "-fno-sanitize-recover=undefined", "-I" + CSRC,
                            os.path.join(HERE, "dma_range_model.cpp"), "-o", exe])
     res = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert res.returncode == 0 and res.stdout.strip().endswith("ok"), res.stdout + res.stderr

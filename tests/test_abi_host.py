@@ -198,3 +198,17 @@ def test_noalloc_validation(L):
     assert f(FAKE, FAKE, 8, 0.1, FAKE, MIS, None) == 3            # misaligned bf16 output
     assert f(FAKE, FAKE, 8, float("inf"), FAKE, FAKE, None) == 5  # non-finite learning rate
     assert f(None, None, 0, 0.1, None, None, None) == 0           # empty: nothing to do
+
+
+def test_launch_failure_maps_to_err_launch(L):
+    # With no HIP device the runtime rejects every launch: calls whose arguments pass validation
+    # must then report PURO_ERR_LAUNCH (4) rather than succeed or crash. On a machine with a
+    # device these arguments would reach a kernel, so the test only runs where there is none.
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a HIP device is present: these fake pointers would be dereferenced")
+    assert L.puro_quant_act_1x128(FAKE, 128, 128, FAKE, FAKE, None) == 4
+    assert L.puro_quant_dual_1x128(FAKE, 128, 128, FAKE, FAKE, FAKE, FAKE, None) == 4
+    assert L.puro_fp8_gemm_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 128, 128, 128, None) == 4
+    assert L.puro_fp8_gemm_wgrad(FAKE, FAKE, FAKE, FAKE, FAKE, 8192, 2048, 2048, 0, None) == 4
+    assert L.puro_hyperball_step_noalloc(FAKE, FAKE, 8, 0.1, FAKE, FAKE, None) == 4

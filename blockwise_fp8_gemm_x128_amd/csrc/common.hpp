@@ -74,6 +74,40 @@ __device__ __forceinline__ void group_scale(float amax, float& s, float& r) {
   }
 }
 
+// Cross-lane maxima of non-negative fp32 values (magnitudes), in registers: for such values the
+// order of the bit patterns as unsigned integers is the order of the values, so an integer max
+// of the patterns is exact and needs no NaN handling (inputs are finite by contract).
+__device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_mov_dpp(static_cast<int>(v), kCtrl, 0xF, 0xF, false));
+}
+// Max over the 16 lanes of each row of the wave (lanes 16k .. 16k+15): swap neighbours, swap
+// pairs, mirror halves of 8, mirror the row.
+__device__ __forceinline__ float row16_max(float m) {
+  uint32_t u = __float_as_uint(m);
+  u = umax32(u, dpp<0xB1>(u));   // quad_perm [1,0,3,2]
+  u = umax32(u, dpp<0x4E>(u));   // quad_perm [2,3,0,1]
+  u = umax32(u, dpp<0x141>(u));  // row_half_mirror
+  u = umax32(u, dpp<0x140>(u));  // row_mirror
+  return __uint_as_float(u);
+}
+// Max over lanes l, l^16, l^32, l^48 (across the four rows of the wave).
+__device__ __forceinline__ float across_rows_max(float m) {
+  uint32_t u = __float_as_uint(m);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  u = umax32(p16[0], p16[1]);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(umax32(p32[0], p32[1]));
+}
+// Max over lanes l, l^8, l^16, ..., l^56 (the eight lanes of a wave that share l mod 8).
+__device__ __forceinline__ float stride8_max(float m) {
+  uint32_t u = __float_as_uint(m);
+  u = umax32(u, dpp<0x128>(u));  // row_ror:8 (lane l and l^8 within a row)
+  return across_rows_max(__uint_as_float(u));
+}
+
 // Power-of-two scale of a group: s = 2^e for the least integer e with 448 * 2^e >= amax, raised
 // to -127 when smaller, and r = 2^-e exactly, so x * r is exact; an all-zero group gets
 // s = r = 1. With amax = (1 + f) * 2^(E - 127) (E the biased exponent field, f the fraction)

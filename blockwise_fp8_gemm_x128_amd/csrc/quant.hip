@@ -67,8 +67,7 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(const uint16_t* __
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) m = fmaxf(m, __builtin_fabsf(f[i]));
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
+    m = row16_max(m);
     float sc, r;
     scale_rule<kPow2>(m, sc, r);
     uint2 out;
@@ -203,8 +202,7 @@ __global__ __launch_bounds__(512) void quant_dual_1x128_kernel(
       float m = 0.0f;
 #pragma unroll
       for (int i = 0; i < 8; ++i) m = fmaxf(m, __builtin_fabsf(f[i]));
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
+      m = row16_max(m);
       float sc, rc;
       scale_rule<kPow2>(m, sc, rc);
       uint2 out;
@@ -220,20 +218,28 @@ __global__ __launch_bounds__(512) void quant_dual_1x128_kernel(
   const int pair = lane & 7, g = lane >> 3;
   {
     const int dc = w * 8 + pair;  // dword column: tile columns 2*dc, 2*dc+1
+    // Lanes of groups g and g + 4 would hit the same LDS banks row for row (16 rows x 65
+    // dwords apart = 16 banks, mod 64); the upper four groups therefore walk their 16 rows
+    // starting at row 8, so every read instruction touches 64 distinct banks. d[i] holds row
+    // 16g + ((i + rot) mod 16), and the encoded halves are swapped back below.
+    const int rot = (g >> 2) << 3;
+    const uint32_t* grp = tile + 16 * g * kDualPitch + dc;
+    const uint32_t* lo = grp + rot * kDualPitch;        // rows rot .. rot + 7
+    const uint32_t* hi = grp + (8 - rot) * kDualPitch;  // the other 8 rows
     uint32_t d[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) d[i] = tile[(16 * g + i) * kDualPitch + dc];
+    for (int i = 0; i < 8; ++i) {
+      d[i] = lo[i * kDualPitch];
+      d[8 + i] = hi[i * kDualPitch];
+    }
     float m0v = 0.0f, m1v = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       m0v = fmaxf(m0v, __builtin_fabsf(bf16_lo(d[i])));
       m1v = fmaxf(m1v, __builtin_fabsf(bf16_hi(d[i])));
     }
-#pragma unroll
-    for (int off = 8; off < 64; off <<= 1) {
-      m0v = fmaxf(m0v, __shfl_xor(m0v, off, 64));
-      m1v = fmaxf(m1v, __shfl_xor(m1v, off, 64));
-    }
+    m0v = stride8_max(m0v);
+    m1v = stride8_max(m1v);
     float s0, r0, s1, r1;
     scale_rule<kPow2>(m0v, s0, r0);
     scale_rule<kPow2>(m1v, s1, r1);
@@ -246,6 +252,10 @@ __global__ __launch_bounds__(512) void quant_dual_1x128_kernel(
     o1.y = e4m3x4(bf16_hi(d[4]) * r1, bf16_hi(d[5]) * r1, bf16_hi(d[6]) * r1, bf16_hi(d[7]) * r1);
     o1.z = e4m3x4(bf16_hi(d[8]) * r1, bf16_hi(d[9]) * r1, bf16_hi(d[10]) * r1, bf16_hi(d[11]) * r1);
     o1.w = e4m3x4(bf16_hi(d[12]) * r1, bf16_hi(d[13]) * r1, bf16_hi(d[14]) * r1, bf16_hi(d[15]) * r1);
+    if (rot) {  // back to row order: rows 0-7 of the group are in the upper eight bytes
+      o0 = make_uint4(o0.z, o0.w, o0.x, o0.y);
+      o1 = make_uint4(o1.z, o1.w, o1.x, o1.y);
+    }
     const int64_t col = c0 + 2 * dc;
     *reinterpret_cast<uint4*>(qt + col * rows + m0 + 16 * g) = o0;
     *reinterpret_cast<uint4*>(qt + (col + 1) * rows + m0 + 16 * g) = o1;

@@ -75,7 +75,12 @@ enum Mode : int { kFwd = 0, kDgrad = 1, kWgrad = 2 };
 
 constexpr int kChunk = 128;       // reduction chunk = quantisation group
 constexpr int kSlab = 128 * 128;  // bytes of one 128-row x 128-byte staged slab
-constexpr int kGroupRows = 8;     // tile-rows per band of the block order
+// Tile-rows per band of the block order: 4 for the forward and data-gradient 256x256 tiles,
+// 8 for the others (measured on the linear-stack step).
+template <int kMode, int BM>
+constexpr int group_rows() {
+  return (kMode != kWgrad && BM == 256) ? 4 : 8;
+}
 
 template <int kMode, int BM_, int BN_, int WAVES_M_, int WAVES_N_, bool kPow2_ = false>
 struct Cfg {
@@ -83,6 +88,7 @@ struct Cfg {
   static constexpr bool kPow2 = kPow2_;  // power-of-two scales, applied by the matrix cores
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int kGroupRows = group_rows<kMode, BM_>();
   static constexpr int kWaves = WAVES_M * WAVES_N;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -581,10 +587,10 @@ __device__ __forceinline__ void tile_origin(int64_t I, int64_t J, int64_t& i0, i
   const int64_t nwg = tiles_i * tiles_j;
   int64_t b = blockIdx.x;
   if ((nwg & 7) == 0) b = (b & 7) * (nwg >> 3) + (b >> 3);
-  const int64_t band = b / (kGroupRows * tiles_j);
-  const int64_t band_rows = imin64(kGroupRows, tiles_i - band * kGroupRows);
-  const int64_t local = b - band * kGroupRows * tiles_j;
-  const int64_t ti = band * kGroupRows + local % band_rows;
+  const int64_t band = b / (C::kGroupRows * tiles_j);
+  const int64_t band_rows = imin64(C::kGroupRows, tiles_i - band * C::kGroupRows);
+  const int64_t local = b - band * C::kGroupRows * tiles_j;
+  const int64_t ti = band * C::kGroupRows + local % band_rows;
   const int64_t tj = local / band_rows;
   i0 = uniform64(ti * C::BM);
   j0 = uniform64(tj * C::BN);

@@ -8,6 +8,9 @@
         WRITE_SIZE, KiB per dispatch), each scaled by the same counter's reading for a plain
         copy of known size (bench.py --copy-calibration), with one `traffic-record:` line per
         function that bench.py reads back while the function's sources are unchanged
+    python -m blockwise_fp8_gemm_x128_amd.profiling sq CSV [CSV ...]
+        ratios of shader-sequencer counters (instruction mix, matrix-core and LDS activity,
+        waits) per GEMM function, from one or more counter passes
 
 Kernel names are reduced to the names bench.py accounts launches under (the function name,
 with "(columns only)" for the transposed quantiser's instance of the two-orientation kernel and
@@ -161,6 +164,67 @@ def traffic_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv, title: str,
     return "\n".join(lines) + "\n"
 
 
+def _per_dispatch(path: str):
+    """{dispatch id: {'fn': function, counter: value, ...}} of a counter CSV (this library's
+    kernels only)."""
+    out = {}
+    for r in _rows(path):
+        fn = function_of(r["Kernel_Name"])
+        if not fn:
+            continue
+        d = out.setdefault(r["Dispatch_Id"], {"fn": fn})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def sq_summary(csvs, title: str) -> str:
+    """Ratios of shader-sequencer counters per GEMM function, each summed over the function's
+    dispatches in every counter pass given."""
+    agg = {}
+    for path in csvs:
+        for d in _per_dispatch(path).values():
+            a = agg.setdefault(d["fn"], {"n": {}})
+            a["n"][path] = a["n"].get(path, 0) + 1
+            for k, v in d.items():
+                if k != "fn":
+                    a[k] = a.get(k, 0.0) + v
+
+    def ratio(a, num, den):
+        return a[num] / a[den] if num in a and a.get(den) else float("nan")
+
+    lines = [title, "",
+             "Ratios (instruction counts or cycles, summed over the function's dispatches):",
+             "  VALU/MFMA   SQ_INSTS_VALU / SQ_INSTS_MFMA (the promotion alone: 4 FMAs and 1/4",
+             "              multiply per MFMA for fwd/dgrad, 4 multiplies + 4 FMAs for wgrad)",
+             "  LDS/MFMA    SQ_INSTS_LDS / SQ_INSTS_MFMA",
+             "  SALU/MFMA   SQ_INSTS_SALU / SQ_INSTS_MFMA",
+             "  confl/LDS   SQ_LDS_BANK_CONFLICT cycles per LDS instruction",
+             "  MFMA busy   SQ_VALU_MFMA_BUSY_CYCLES / (4 x SQ_BUSY_CU_CYCLES): share of SIMD",
+             "              cycles the matrix core is busy while the CUs are busy",
+             "  LDS active  SQ_LDS_IDX_ACTIVE / SQ_BUSY_CU_CYCLES",
+             "  wait        SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (share of wave cycles waiting on a",
+             "              memory counter)",
+             "  waitLDS     SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES", "",
+             f"  {'function':28s} {'n':>3s} {'VALU/MFMA':>9s} {'LDS/MFMA':>8s} {'SALU/MFMA':>9s} "
+             f"{'confl/LDS':>9s} "
+             f"{'MFMA busy':>9s} {'LDS active':>10s} {'wait':>6s} {'waitLDS':>7s}"]
+    for fn in sorted(agg):
+        if not fn.startswith("gemm"):
+            continue
+        a = agg[fn]
+        busy = a.get("SQ_BUSY_CU_CYCLES")
+        lines.append(
+            f"  {fn:28s} {max(a['n'].values()):3d} {ratio(a, 'SQ_INSTS_VALU', 'SQ_INSTS_MFMA'):9.2f} "
+            f"{ratio(a, 'SQ_INSTS_LDS', 'SQ_INSTS_MFMA'):8.2f} "
+            f"{ratio(a, 'SQ_INSTS_SALU', 'SQ_INSTS_MFMA'):9.2f} "
+            f"{ratio(a, 'SQ_LDS_BANK_CONFLICT', 'SQ_INSTS_LDS'):9.3f} "
+            f"{(a['SQ_VALU_MFMA_BUSY_CYCLES'] / (4 * busy) if busy else float('nan')):9.3f} "
+            f"{(a['SQ_LDS_IDX_ACTIVE'] / busy if busy and 'SQ_LDS_IDX_ACTIVE' in a else float('nan')):10.3f} "
+            f"{ratio(a, 'SQ_WAIT_INST_ANY', 'SQ_WAVE_CYCLES'):6.3f} "
+            f"{ratio(a, 'SQ_WAIT_INST_LDS', 'SQ_WAVE_CYCLES'):7.3f}")
+    return "\n".join(lines) + "\n"
+
+
 def main(argv=None):
     p = argparse.ArgumentParser()
     sub = p.add_subparsers(dest="cmd", required=True)
@@ -176,8 +240,13 @@ def main(argv=None):
     r.add_argument("--bench-log", default=None,
                    help="bench.py output of the counter run, for the algorithmic bytes")
     r.add_argument("--title", default="HBM traffic per launch per function")
+    q = sub.add_parser("sq")
+    q.add_argument("csvs", nargs="+")
+    q.add_argument("--title", default="Shader-sequencer counters per GEMM function")
     a = p.parse_args(argv)
-    if a.cmd == "time":
+    if a.cmd == "sq":
+        sys.stdout.write(sq_summary(a.csvs, a.title))
+    elif a.cmd == "time":
         sys.stdout.write(time_summary(a.stats_csv, a.bench_log, a.title))
     else:
         alg = None

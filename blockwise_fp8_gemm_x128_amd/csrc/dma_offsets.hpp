@@ -4,9 +4,12 @@
 //
 // A raw buffer load reads zero when its offset lies at or beyond the resource's byte count.
 // Whether the scalar offset operand takes part in that check is not something to rely on, so
-// every load here passes its whole offset as the per-lane offset (scalar offset 0): the check
-// then covers the row and column the lane addresses, and the invalid part of an edge tile reads
-// zeros without touching memory past the tensor.
+// every load of a tile that lies partly outside its operand passes its whole offset as the
+// per-lane offset (scalar offset 0): the check then covers the row and column the lane
+// addresses, and the invalid part of an edge tile reads zeros without touching memory past the
+// tensor. Row-major tiles wholly inside their operand address only its own bytes: there the
+// lane part (rows_lane) is the per-lane offset and the wave-uniform part (rows_group) the scalar
+// one, and no range check is needed.
 #pragma once
 #include <stdint.h>
 

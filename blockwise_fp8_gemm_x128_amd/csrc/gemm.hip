@@ -139,10 +139,14 @@ __device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b) {
 }
 
 // 16 bytes per lane from global memory straight into LDS through a buffer resource: lane i's
-// bytes (at base + voff_i) land at lds_dst + 16 * i (lds_dst is wave-uniform). The whole offset
-// is the per-lane one and the scalar offset is 0, so the range check sees the row (and column)
-// each lane addresses: offsets at or beyond the resource's byte count read as zero, which covers
-// the invalid part of edge tiles without clamping and without reading past a tensor's end.
+// bytes (at base + voff_i + soff) land at lds_dst + 16 * i (lds_dst and soff are wave-uniform).
+// Tiles that lie partly outside an operand pass the whole offset per lane (soff = 0), so the
+// range check sees the row (and column) each lane addresses: offsets at or beyond the resource's
+// byte count read as zero, which covers the invalid part of edge tiles without clamping and
+// without reading past a tensor's end. Tiles wholly inside the operand address only its own
+// bytes and need no check: in the weight-gradient kernels their loads keep the wave-uniform part
+// of the offset in soff, which saves a vector add per load (those kernels are bound by their
+// vector ALU).
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;  // raw, untyped 32-bit-offset buffer (gfx9 family)
 
@@ -152,9 +156,10 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
                                            kRsrcWord3);
 }
 
-__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, lds_u8* lds_dst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 16, static_cast<int>(voff), 0,
-                                           0, 0);
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, lds_u8* lds_dst,
+                                      uint32_t soff = 0) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 16, static_cast<int>(voff),
+                                           static_cast<int>(soff), 0, 0);
 }
 
 // A chunk's lane offset: the lane part plus the chunk's column offset, hidden from the
@@ -166,7 +171,7 @@ __device__ __forceinline__ uint32_t chunk_lane_offset(uint32_t lane_part, int64_
   return v;
 }
 
-template <class C>
+template <class C, bool kScalarRowOffsets_ = C::mode == kWgrad>
 struct Loader {
   // 8-wave tiles alternate the DMA between the two halves of the block by chunk parity (waves w
   // and w + 4 share a SIMD, so while one of them is held up feeding the memory pipeline the
@@ -175,6 +180,12 @@ struct Loader {
   static constexpr int kIssuers = kPingPong ? C::kWaves / 2 : C::kWaves;
   static constexpr int kAInstr = C::BM / 8 / kIssuers;  // DMA instructions per issuing wave, A
   static constexpr int kBInstr = C::BN / 8 / kIssuers;  // and B tile
+  // Interior tiles take the scalar-offset form in the one-group weight-gradient kernels only.
+  // Measured on MI355X (same box, alternated): the 4-wave 128x128 weight gradient 3.4 % faster,
+  // 192x256 1.7 %, 256x192 0.5 %; the split-reduction kernel 3.8 % slower (38 scalar registers
+  // spilled to vector lanes instead of 25), the forward and data-gradient kernels 0.5 % and
+  // 1.6 % slower (0 -> 19 and 19 -> 34 spilled).
+  static constexpr bool kScalarRowOffsets = kScalarRowOffsets_;
 
   // Instruction k of issuing wave w copies staged rows [8q, 8q+8), q = w + kIssuers*k; lane l
   // takes row 8q + l/8 and physical piece l%8, i.e. logical piece (l%8) ^ swz(row). For
@@ -189,6 +200,7 @@ struct Loader {
   int64_t I, J, L, i0, j0;
   rsrc_t ra, rb;          // per-tile resources (A, and row-major B)
   uint32_t a_voff, b_voff;
+  bool a_inside, b_inside;  // the tile's rows of A (of row-major B) all lie inside the operand
   uint32_t bt_voff[kBInstr];  // reduction-major B: per instruction
   int wave, lane;
   const float* sb_block;  // block modes: the wave's block scale of chunk 0 (uniform)
@@ -203,6 +215,8 @@ struct Loader {
     const int xr = swz_rows(8 * w + r8);  // = swz_rows(8q + r8) for every instruction k
     ra = make_rsrc(A + i0 * L, (I - i0) * L);
     a_voff = dma::rows_lane(r8, p8 ^ xr, L);
+    a_inside = kScalarRowOffsets && I - i0 >= C::BM;
+    b_inside = kScalarRowOffsets && J - j0 >= C::BN;
     if (C::kBTrans) {
 #pragma unroll
       for (int k = 0; k < kBInstr; ++k) {
@@ -250,11 +264,19 @@ struct Loader {
       // The same share written out with the wave index itself: routed through the issuing-wave
       // functions below, the compiler merged the two scale loads of the 4-wave weight-gradient
       // kernel into one with a selected source and that kernel ran 7-9 % slower (MI355X).
-      const uint32_t av = chunk_lane_offset(a_voff, c);
+      if (a_inside) {
 #pragma unroll
-      for (int k = 0; k < kAInstr; ++k) {
-        const int q = wave + C::kWaves * k;
-        dma16(ra, av + dma::rows_group(q, L, 0), stage + C::kAOff + 8 * q * kChunk);
+        for (int k = 0; k < kAInstr; ++k) {
+          const int q = wave + C::kWaves * k;
+          dma16(ra, a_voff, stage + C::kAOff + 8 * q * kChunk, dma::rows_group(q, L, c));
+        }
+      } else {
+        const uint32_t av = chunk_lane_offset(a_voff, c);
+#pragma unroll
+        for (int k = 0; k < kAInstr; ++k) {
+          const int q = wave + C::kWaves * k;
+          dma16(ra, av + dma::rows_group(q, L, 0), stage + C::kAOff + 8 * q * kChunk);
+        }
       }
       if (C::kBTrans) {
         // staged B = BN/128 slabs of 128 reduction rows x 128 columns; slab s holds columns
@@ -265,6 +287,12 @@ struct Loader {
         for (int k = 0; k < kBInstr; ++k) {
           const int q = wave + C::kWaves * k;
           dma16(rbc, bt_voff[k], stage + C::kBOff + 8 * q * kChunk);
+        }
+      } else if (b_inside) {
+#pragma unroll
+        for (int k = 0; k < kBInstr; ++k) {
+          const int q = wave + C::kWaves * k;
+          dma16(rb, b_voff, stage + C::kBOff + 8 * q * kChunk, dma::rows_group(q, L, c));
         }
       } else {
         const uint32_t bv = chunk_lane_offset(b_voff, c);
@@ -294,11 +322,19 @@ struct Loader {
   // The share of issuing wave w (of kIssuers) in an 8-wave block: the A rows with the scale rows,
   // and the B rows.
   __device__ __forceinline__ void issue_as_a(lds_u8* stage, int64_t c, int w) const {
-    const uint32_t av = chunk_lane_offset(a_voff, c);
+    if (a_inside) {
 #pragma unroll
-    for (int k = 0; k < kAInstr; ++k) {
-      const int q = w + kIssuers * k;
-      dma16(ra, av + dma::rows_group(q, L, 0), stage + C::kAOff + 8 * q * kChunk);
+      for (int k = 0; k < kAInstr; ++k) {
+        const int q = w + kIssuers * k;
+        dma16(ra, a_voff, stage + C::kAOff + 8 * q * kChunk, dma::rows_group(q, L, c));
+      }
+    } else {
+      const uint32_t av = chunk_lane_offset(a_voff, c);
+#pragma unroll
+      for (int k = 0; k < kAInstr; ++k) {
+        const int q = w + kIssuers * k;
+        dma16(ra, av + dma::rows_group(q, L, 0), stage + C::kAOff + 8 * q * kChunk);
+      }
     }
     // scale rows: all 64 lanes (no divergence); lanes past the tile's rows read zeros
     if (w == 0)
@@ -318,6 +354,12 @@ struct Loader {
       for (int k = 0; k < kBInstr; ++k) {
         const int q = w + kIssuers * k;
         dma16(rbc, bt_voff[k], stage + C::kBOff + 8 * q * kChunk);
+      }
+    } else if (b_inside) {
+#pragma unroll
+      for (int k = 0; k < kBInstr; ++k) {
+        const int q = w + kIssuers * k;
+        dma16(rb, b_voff, stage + C::kBOff + 8 * q * kChunk, dma::rows_group(q, L, c));
       }
     } else {
       const uint32_t bv = chunk_lane_offset(b_voff, c);
@@ -812,7 +854,7 @@ __device__ __forceinline__ void gemm_body_k2(const uint8_t* __restrict__ A,
   const int wm = wave / C::WAVES_N, wn = wave % C::WAVES_N;
   const int64_t nk = L / kChunk;
 
-  Loader<C> ld;
+  Loader<C, false> ld;  // the scalar-offset form spills here (see Loader)
   ld.A = A;
   ld.B = B;
   ld.sA = sA;

@@ -10,8 +10,12 @@
 //     element when its column is inside the tensor, and the last row's columns past the end are
 //     out of range;
 //   - a scale-row load is in range exactly when its four scales belong to valid rows.
-// The model of the check: a lane's 16 bytes are read when offset < the resource's byte count
-// (scalar offset 0, so there is no question of whether the scalar offset is checked).
+// The model of the check: a lane's 16 bytes are read when offset < the resource's byte count.
+// Edge tiles pass the whole offset per lane (scalar offset 0), so there is no question of
+// whether the scalar offset is checked. Row-major tiles that lie wholly inside their operand
+// keep the row-group and chunk part in the scalar offset; for them the model checks that every
+// lane addresses the expected element inside the tensor and is in range whether the check
+// includes the scalar offset or not.
 // Prints "ok" and exits 0, or prints the first violations and exits 1.
 #include <cstdint>
 #include <cstdio>
@@ -51,9 +55,19 @@ static void check_rows(int64_t T, int64_t L, int tile, int issuers) {
             const int xr = swz_rows(8 * w + r8);  // the kernel's per-lane swizzle
             if (xr != swz_rows(8 * q + r8)) fail("row swizzle", q, r8, w, k);
             const int piece = p8 ^ xr;
+            const int64_t row = t0 + 8 * q + r8;
+            if (T - t0 >= tile) {
+              // interior tile: lane part per lane, row group and chunk in the scalar offset
+              const uint32_t lv = rows_lane(r8, piece, L), so = rows_group(q, L, c);
+              const int64_t addr = t0 * L + int64_t(lv) + int64_t(so);
+              if (addr != row * L + c * 128 + 16 * piece) fail("inner address", row, c, piece, addr);
+              if (addr < 0 || addr + 16 > T * L) fail("inner past end", T, L, row, addr);
+              if (!(lv < nrec) || !(int64_t(lv) + int64_t(so) < int64_t(nrec)))
+                fail("inner range", T, L, row, int64_t(lv) + int64_t(so));
+              continue;
+            }
             const uint32_t voff = rows_lane(r8, piece, L) + rows_group(q, L, 0) +
                                   static_cast<uint32_t>(c * 128);
-            const int64_t row = t0 + 8 * q + r8;
             const bool in_range = voff < nrec;
             if (in_range != (row < T)) fail("row range", T, L, row, voff);
             if (in_range) {

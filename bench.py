@@ -70,6 +70,10 @@ def parse():
                         "projection outlier stress; all: c1, c2, c3), one JSON line each")
     p.add_argument("--no-copy-ceiling", action="store_true",
                    help="skip the same-run copy ceiling and per-shape quantiser/copy rates")
+    p.add_argument("--ceiling", action="store_true",
+                   help="only run the matrix-core microbenchmark (libpuro_probe.so): the MFMA "
+                        "instruction's rate on register operands, without and with the GEMMs' "
+                        "promotion, on zero, random and quantised-data codes, and the shader clock")
     return p.parse_args()
 
 
@@ -691,10 +695,83 @@ def config_cpu_baseline(name, host, M, backward):
                        f"linearly to all rows") + "; every quantiser at full size (timed apart)"}
 
 
+def mfma_ceiling(iters: int = 100000):
+    """Register-only rate of the GEMMs' instruction (v_mfma_f32_16x16x128_f8f6f4), from the
+    microbenchmark in csrc/ceiling.hip: 8 independent products per round on operands loaded
+    once, in three modes (0: accumulate in the matrix core; 1: + 4 FMAs per product, the
+    forward/data-gradient promotion; 2: + 4 multiplies and 4 FMAs, the weight-gradient one), at
+    2 and 4 waves per SIMD (256 or 512 blocks of 8 waves), on three operand patterns. The rate
+    is flops over the launch's HIP-event duration; the clock is the median wave's shader-clock
+    cycles (s_memtime) over the same duration, and `ticks_mhz` the constant-rate counter's
+    (s_memrealtime) rate as a check on the timing."""
+    import ctypes
+
+    import torch
+    from blockwise_fp8_gemm_x128_amd import binding as B
+    from blockwise_fp8_gemm_x128_amd.build import PROBE_PATH
+
+    if not os.path.exists(PROBE_PATH):
+        raise SystemExit(f"{PROBE_PATH} is missing: build first (python -c 'import "
+                         "__graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(PROBE_PATH)
+    fn = lib.puro_probe_mfma
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                   ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                   ctypes.c_void_p]
+    st = torch.cuda.current_stream()
+    nbytes = 1 << 20
+    g = torch.Generator().manual_seed(7)
+    rnd = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=g)
+    rnd[(rnd & 0x7F) == 0x7F] = 0x7E  # no NaN codes (S.1111.111)
+    x = (torch.randn((nbytes // 128, 128), generator=g) * 1.0).to(torch.bfloat16).cuda()
+    xq, _ = B.puro_quant_act_1x128(x)
+    patterns = {"zero": torch.zeros(nbytes, dtype=torch.uint8, device="cuda"),
+                "random E4M3 codes": rnd.cuda(),
+                "quantised N(0,1) bf16": xq.reshape(-1).contiguous()}
+    modes = {0: "MFMA chain", 1: "+ 4 FMAs per product", 2: "+ 4 multiplies + 4 FMAs"}
+    out = {}
+    for pname, codes in patterns.items():
+        for wps in (2, 4):
+            blocks = 256 * wps // 2
+            waves = blocks * 8
+            cyc = torch.zeros(waves, dtype=torch.int64, device="cuda")
+            tck = torch.zeros(waves, dtype=torch.int64, device="cuda")
+            sink = torch.zeros(waves * 64, dtype=torch.float32, device="cuda")
+            for mode, mname in modes.items():
+                def launch(n):
+                    rc = fn(codes.data_ptr(), nbytes, blocks, 8, n, mode, cyc.data_ptr(),
+                            tck.data_ptr(), sink.data_ptr(), ctypes.c_void_p(st.cuda_stream))
+                    if rc != 0:
+                        raise RuntimeError(f"puro_probe_mfma returned {rc}")
+                launch(iters // 10)
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+                launch(iters)
+                e1.record(st)
+                torch.cuda.synchronize()
+                sec = e0.elapsed_time(e1) * 1e-3
+                flops = waves * iters * 8 * 2.0 * 16 * 16 * 128
+                clk = float(cyc.double().median()) / sec / 1e9
+                pf = flops / sec / 1e15
+                out[f"{pname} | {wps} waves/SIMD | {mname}"] = {
+                    "pflops": pf, "frac_of_5pf": pf / 5.0, "ms": sec * 1e3,
+                    "clock_ghz": clk, "frac_at_that_clock": pf / (5.0 * clk / 2.4),
+                    "ticks_mhz": float(tck.double().median()) / sec / 1e6}
+    print(json.dumps({"mfma_ceiling": out, "iters": iters,
+                      "instruction": "v_mfma_f32_16x16x128_f8f6f4 (E4M3 x E4M3, fp32)",
+                      "peak_assumed": "5.0 PFLOP/s dense FP8 at 2.4 GHz"}), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.ceiling:
+        mfma_ceiling()
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "

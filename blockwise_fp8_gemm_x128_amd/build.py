@@ -14,6 +14,10 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(REPO_DIR, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libpuro.so")
 SOURCES = ["abi.hip", "quant.hip", "gemm.hip", "optim.hip"]
+# The matrix-core microbenchmark that bench.py --ceiling runs; a library of its own, outside the
+# GEMM path.
+PROBE_PATH = os.path.join(PKG_DIR, "libpuro_probe.so")
+PROBE_SOURCES = ["ceiling.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -30,9 +34,9 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = True) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+def _hipcc(sources, out: str, verbose: bool) -> str:
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, *FLAGS, "-I" + INCLUDE, "-I" + CSRC, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -41,11 +45,16 @@ def build(verbose: bool = True) -> str:
     noise = [l for l in res.stderr.splitlines() if l.strip() and "packed-fp32-ops" not in l]
     if res.returncode != 0:
         sys.stderr.write(res.stderr)
-        raise RuntimeError("hipcc failed building libpuro.so")
+        raise RuntimeError("hipcc failed building " + os.path.basename(out))
     if noise and verbose:
         sys.stderr.write("\n".join(noise) + "\n")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = True) -> str:
+    _hipcc(PROBE_SOURCES, PROBE_PATH, verbose)
+    return _hipcc(SOURCES, LIB_PATH, verbose)
 
 
 if __name__ == "__main__":

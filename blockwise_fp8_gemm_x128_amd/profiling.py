@@ -8,6 +8,9 @@
         WRITE_SIZE, KiB per dispatch), each scaled by the same counter's reading for a plain
         copy of known size (bench.py --copy-calibration), with one `traffic-record:` line per
         function that bench.py reads back while the function's sources are unchanged
+    python -m blockwise_fp8_gemm_x128_amd.profiling ceiling TRACE_CSV BENCH_LOG
+        the matrix-core microbenchmark (bench.py --ceiling) under the kernel trace: rocprof
+        duration and rate of each timed probe launch beside the bench's own figures
     python -m blockwise_fp8_gemm_x128_amd.profiling sq CSV [CSV ...]
         ratios of shader-sequencer counters (instruction mix, matrix-core and LDS activity,
         waits) per GEMM function, from one or more counter passes
@@ -225,6 +228,33 @@ def sq_summary(csvs, title: str) -> str:
     return "\n".join(lines) + "\n"
 
 
+def ceiling_summary(trace_csv: str, log_path: str, title: str) -> str:
+    """The matrix-core microbenchmark (bench.py --ceiling) under the kernel trace: each timed
+    probe launch's rocprof duration beside the bench's own figures for it. The probe launches
+    come in the bench's order, a short warm-up launch before each timed one."""
+    b = bench_json(log_path) or {}
+    rows = b.get("mfma_ceiling", {})
+    iters = b.get("iters", 0)
+    launches = [r for r in _rows(trace_csv) if "mfma_probe_kernel" in r["Kernel_Name"]]
+    launches.sort(key=lambda r: int(r["Dispatch_Id"]))
+    timed = launches[1::2]
+    lines = [title, "",
+             f"  {'operands | waves per SIMD | loop':66s} {'rocprof ms':>10s} {'PF':>6s} "
+             f"{'of 5 PF':>7s} {'events PF':>9s} {'clock GHz':>9s}"]
+    for (name, v), r in zip(rows.items(), timed):
+        ms = (float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) / 1e6
+        waves = int(r["Grid_Size_X"]) // 64
+        pf = waves * iters * 8 * 2.0 * 16 * 16 * 128 / (ms * 1e-3) / 1e15
+        clk = v["clock_ghz"] * 100.0 / v["ticks_mhz"] if v.get("ticks_mhz") else float("nan")
+        lines.append(f"  {name:66s} {ms:10.2f} {pf:6.2f} {pf / 5.0:7.3f} {v['pflops']:9.2f} "
+                     f"{clk:9.2f}")
+    lines += ["",
+              "PF: flops of the timed launch over its rocprof duration ('events PF': over the HIP-event",
+              "duration of the bench's own run). clock: the median wave's shader-clock cycles",
+              "(s_memtime) over its constant-rate ticks (s_memrealtime, 100 MHz) across the loop."]
+    return "\n".join(lines) + "\n"
+
+
 def main(argv=None):
     p = argparse.ArgumentParser()
     sub = p.add_subparsers(dest="cmd", required=True)
@@ -240,11 +270,17 @@ def main(argv=None):
     r.add_argument("--bench-log", default=None,
                    help="bench.py output of the counter run, for the algorithmic bytes")
     r.add_argument("--title", default="HBM traffic per launch per function")
+    c = sub.add_parser("ceiling")
+    c.add_argument("trace_csv")
+    c.add_argument("log")
+    c.add_argument("--title", default="Matrix-core microbenchmark")
     q = sub.add_parser("sq")
     q.add_argument("csvs", nargs="+")
     q.add_argument("--title", default="Shader-sequencer counters per GEMM function")
     a = p.parse_args(argv)
-    if a.cmd == "sq":
+    if a.cmd == "ceiling":
+        sys.stdout.write(ceiling_summary(a.trace_csv, a.log, a.title))
+    elif a.cmd == "sq":
         sys.stdout.write(sq_summary(a.csvs, a.title))
     elif a.cmd == "time":
         sys.stdout.write(time_summary(a.stats_csv, a.bench_log, a.title))

@@ -212,3 +212,24 @@ def test_launch_failure_maps_to_err_launch(L):
     assert L.puro_fp8_gemm_fwd(FAKE, FAKE, FAKE, FAKE, FAKE, 128, 128, 128, None) == 4
     assert L.puro_fp8_gemm_wgrad(FAKE, FAKE, FAKE, FAKE, FAKE, 8192, 2048, 2048, 0, None) == 4
     assert L.puro_hyperball_step_noalloc(FAKE, FAKE, 8, 0.1, FAKE, FAKE, None) == 4
+
+
+def test_probe_library_validation():
+    """The matrix-core microbenchmark (libpuro_probe.so, bench.py --ceiling) loads, exports its
+    one function and rejects bad arguments before any launch."""
+    from blockwise_fp8_gemm_x128_amd.build import PROBE_PATH, build
+    if not os.path.exists(PROBE_PATH):
+        build(verbose=False)
+    P = ctypes.CDLL(PROBE_PATH)
+    fn = P.puro_probe_mfma
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                   ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                   ctypes.c_void_p]
+    p = 1 << 16  # a fake, 64-byte aligned address: validation never dereferences it
+    good = (p, 4096, 1, 8, 1, 0, p, p, p, None)
+    for i, bad in ((0, None), (1, 4000), (1, 4100), (0, p + 32), (2, 0), (3, 17), (3, 0),
+                   (4, 0), (5, 3), (5, -1), (6, None), (7, None), (8, None)):
+        args = list(good)
+        args[i] = bad
+        assert fn(*args) == 1, (i, bad)

@@ -5,9 +5,9 @@ import this package. The GPU library never does, and nothing here imports the GP
 
 Thin ctypes/numpy wrapper over ``oracle.c`` (plain C, IEEE binary32/64 arithmetic, OpenMP over
 independent groups/rows). The method it follows is stated in the page "Paper walkthrough:
-Puro-2B" (ta-paperlens.web.app), section "Lever 2: use blockwise FP8 from step zero":
-activations and their gradients are scaled per group of 128 along the reduction dimension,
-weights per 128x128 block, and only the linear-layer GEMMs run in FP8.
+Puro-2B" (ta-paperlens.web.app), section "Lever 2: use blockwise FP8 from step zero": the
+linear-layer GEMMs alone take FP8 operands, each with an fp32 scale per local group (a run of
+128 along the GEMM's reduction for X and dY, a 128x128 block for W).
 
 Inputs are bf16 tensors given as numpy ``uint16`` bit patterns (or torch bf16 CPU tensors);
 quantised payloads are ``uint8`` E4M3 codes; scales are ``float32``; GEMM results ``float64``.

@@ -35,6 +35,8 @@ OPT_WORKSPACE_BYTES = 8 * OPT_MAX_BLOCKS + 256  # PURO_OPT_WORKSPACE_BYTES
 SIGNATURES = {
     "puro_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "puro_abi_version": ([], ctypes.c_int),
+    "puro_set_debug": ([ctypes.c_int], None),
+    "puro_debug_level": ([], ctypes.c_int),
     "puro_quant_act_1x128": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "puro_quant_w_128x128": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),
     "puro_quant_transpose": ([_P, _I64, _I64, _P, _P, _P], ctypes.c_int),

@@ -268,6 +268,18 @@ puro_fp8_gemm_dgrad_pow2 = _pow2_variant(puro_fp8_gemm_dgrad)
 puro_fp8_gemm_wgrad_pow2 = _pow2_variant(puro_fp8_gemm_wgrad)
 
 
+def puro_set_debug(level: int) -> None:
+    """Debug level of the library (0: off; 1 or more: every quantiser and GEMM call checks its
+    inputs on the device first and raises PuroError with PURO_ERR_INPUT on data outside the
+    contract)."""
+    lib().puro_set_debug(int(level))
+
+
+def puro_debug_level() -> int:
+    """Current debug level (initially the PURO_DEBUG environment variable, else 0)."""
+    return int(lib().puro_debug_level())
+
+
 def puro_gemm_kernel_name(op: str, M: int, N: int, K: int, pow2: bool = False) -> str:
     """Name of the kernel function puro_fp8_gemm_<op> (op: 'fwd', 'dgrad' or 'wgrad') launches
     for these sizes on the current device, or '' if it would launch nothing."""

@@ -13,7 +13,7 @@ REPO_DIR = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(REPO_DIR, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libpuro.so")
-SOURCES = ["abi.hip", "quant.hip", "gemm.hip", "optim.hip"]
+SOURCES = ["abi.hip", "quant.hip", "gemm.hip", "optim.hip", "debug.hip"]
 # The matrix-core microbenchmark that bench.py --ceiling runs; a library of its own, outside the
 # GEMM path.
 PROBE_PATH = os.path.join(PKG_DIR, "libpuro_probe.so")

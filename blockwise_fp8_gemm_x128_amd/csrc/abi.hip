@@ -9,6 +9,7 @@ extern "C" const char* puro_status_string(int status) {
     case PURO_ERR_ALIGN: return "PURO_ERR_ALIGN: tensor pointer not 16-byte aligned";
     case PURO_ERR_LAUNCH: return "PURO_ERR_LAUNCH: kernel launch failed";
     case PURO_ERR_ARG: return "PURO_ERR_ARG: argument out of range";
+    case PURO_ERR_INPUT: return "PURO_ERR_INPUT: input data outside the contract (debug check)";
     default: return "unknown puro_status";
   }
 }

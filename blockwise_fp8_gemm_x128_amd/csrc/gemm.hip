@@ -53,6 +53,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "debug.hpp"
 #include "dma_offsets.hpp"
 
 namespace puro {
@@ -1132,6 +1133,8 @@ puro_status gemm_fwd(const void* xq, const float* sx, const void* wq, const floa
   PURO_TRY(check_ptr(sw, red_empty));
   PURO_TRY(check_ptr(y, out_empty));
   if (out_empty) return PURO_OK;
+  PURO_TRY(debug::check_operand(xq, M * K, sx, (K / 128) * M, stream));
+  PURO_TRY(debug::check_operand(wq, N * K, sw, (N / 128) * (K / 128), stream));
   if (use_big_tiles(M, N))
     return launch<typename Ks::FwdB>(Ks::fwd_b, xq, sx, wq, sw, y, M, N, K, 0, stream);
   return launch<typename Ks::FwdS>(Ks::fwd_s, xq, sx, wq, sw, y, M, N, K, 0, stream);
@@ -1150,6 +1153,8 @@ puro_status gemm_dgrad(const void* dyq, const float* sdy, const void* wq, const 
   PURO_TRY(check_ptr(sw, red_empty));
   PURO_TRY(check_ptr(dx, out_empty));
   if (out_empty) return PURO_OK;
+  PURO_TRY(debug::check_operand(dyq, M * N, sdy, (N / 128) * M, stream));
+  PURO_TRY(debug::check_operand(wq, N * K, sw, (N / 128) * (K / 128), stream));
   if (use_big_tiles(M, K))
     return launch<typename Ks::DgB>(Ks::dg_b, dyq, sdy, wq, sw, dx, M, K, N, 0, stream);
   return launch<typename Ks::DgS>(Ks::dg_s, dyq, sdy, wq, sw, dx, M, K, N, 0, stream);
@@ -1170,6 +1175,8 @@ puro_status gemm_wgrad(const void* dytq, const float* sdyt, const void* xtq, con
   PURO_TRY(check_ptr(sxt, red_empty));
   PURO_TRY(check_ptr(dw, out_empty));
   if (out_empty) return PURO_OK;
+  PURO_TRY(debug::check_operand(dytq, N * M, sdyt, (M / 128) * N, stream));
+  PURO_TRY(debug::check_operand(xtq, K * M, sxt, (M / 128) * K, stream));
   switch (pick_wgrad_shape(N, K)) {
     case kW256x256:
       return launch<typename Ks::WgB>(Ks::wg_b, dytq, sdyt, xtq, sxt, dw, N, K, M, accumulate,

@@ -14,6 +14,7 @@
 // wave instruction touches whole 128 B (or larger) segments; all per-element arithmetic (widen,
 // |max|, multiply, clamp, packed convert) stays in registers.
 #include "common.hpp"
+#include "debug.hpp"
 
 namespace puro {
 namespace {
@@ -275,6 +276,7 @@ puro_status quant_act_1x128(const void* x, int64_t rows, int64_t cols, void* q, 
   PURO_TRY(check_ptr(q, empty));
   PURO_TRY(check_ptr(s, empty));
   if (empty) return PURO_OK;
+  PURO_TRY(debug::check_bf16(x, rows, cols, debug::kRowGroups, kPow2, stream));
   const int64_t blocks = (rows / kActRowsPerBlock) * (cols / 128);
   if (blocks > INT32_MAX) return PURO_ERR_SHAPE;
   hipLaunchKernelGGL(quant_act_1x128_kernel<kPow2>, dim3(static_cast<uint32_t>(blocks)),
@@ -292,6 +294,7 @@ puro_status quant_w_128x128(const void* w, int64_t n, int64_t k, void* q, float*
   PURO_TRY(check_ptr(q, empty));
   PURO_TRY(check_ptr(s, empty));
   if (empty) return PURO_OK;
+  PURO_TRY(debug::check_bf16(w, n, k, debug::kBlockGroups, kPow2, stream));
   const int64_t blocks = (n / 128) * (k / 128);
   if (blocks > INT32_MAX) return PURO_ERR_SHAPE;
   hipLaunchKernelGGL(quant_w_128x128_kernel<kPow2>, dim3(static_cast<uint32_t>(blocks)),
@@ -309,6 +312,7 @@ puro_status quant_transpose(const void* x, int64_t rows, int64_t cols, void* qt,
   PURO_TRY(check_ptr(qt, empty));
   PURO_TRY(check_ptr(st, empty));
   if (empty) return PURO_OK;
+  PURO_TRY(debug::check_bf16(x, rows, cols, debug::kColGroups, kPow2, stream));
   const int64_t blocks = (rows / 128) * (cols / 128);
   if (blocks > INT32_MAX) return PURO_ERR_SHAPE;
   const auto kernel = quant_dual_1x128_kernel<kPow2, false>;  // column groups only
@@ -329,6 +333,8 @@ puro_status quant_dual_1x128(const void* x, int64_t rows, int64_t cols, void* q,
   PURO_TRY(check_ptr(qt, empty));
   PURO_TRY(check_ptr(st, empty));
   if (empty) return PURO_OK;
+  PURO_TRY(debug::check_bf16(x, rows, cols, debug::kRowGroups | debug::kColGroups, kPow2,
+                             stream));
   const int64_t blocks = (rows / 128) * (cols / 128);
   if (blocks > INT32_MAX) return PURO_ERR_SHAPE;
   const auto kernel = quant_dual_1x128_kernel<kPow2, true>;
@@ -365,6 +371,8 @@ puro_status quant_w_128x128_group(const puro_w_item* items, int count, void* str
   }
   if (used == 0) return PURO_OK;
   if (blocks > INT32_MAX) return PURO_ERR_SHAPE;
+  for (int i = 0; i < used; ++i)
+    PURO_TRY(debug::check_bf16(g.w[i], g.n[i], g.k[i], debug::kBlockGroups, kPow2, stream));
   g.first[used] = blocks;
   g.count = used;
   hipLaunchKernelGGL(quant_w_128x128_group_kernel<kPow2>, dim3(static_cast<uint32_t>(blocks)),

@@ -22,7 +22,8 @@
  *
  * Conventions for every entry point:
  *   - All pointers are DEVICE pointers owned by the caller; the library allocates, frees and
- *     synchronises nothing and keeps no state between calls (calls are thread-safe).
+ *     synchronises nothing and keeps no state between calls (calls are thread-safe), except in
+ *     debug mode (puro_set_debug below), where each call waits for its input checks.
  *   - Every tensor is dense row-major. Tensor pointers must be 16-byte aligned.
  *   - Every dimension must be a multiple of 128 (zero allowed). A call whose output is empty
  *     returns PURO_OK and launches nothing. A GEMM whose reduction dimension is 0 writes zeros
@@ -32,7 +33,7 @@
  *   - Validation is done on the host before anything is enqueued: a failed check returns a
  *     nonzero status and enqueues nothing. A failed launch returns PURO_ERR_LAUNCH.
  *   - Inputs must be finite, and a nonzero group must have amax >= 2^-119 (so that 448/amax is
- *     finite); such inputs are not checked on the device.
+ *     finite); such inputs are checked on the device only in debug mode.
  *   - Output buffers must not overlap inputs.
  */
 #ifndef PURO_H
@@ -49,7 +50,8 @@ typedef enum {
   PURO_ERR_SHAPE = 2,  /* a dimension is negative, not a multiple of 128, or too large */
   PURO_ERR_ALIGN = 3,  /* a tensor pointer is not 16-byte aligned */
   PURO_ERR_LAUNCH = 4, /* the HIP runtime rejected a kernel launch */
-  PURO_ERR_ARG = 5     /* another argument is out of range (e.g. `accumulate` not 0/1) */
+  PURO_ERR_ARG = 5,    /* another argument is out of range (e.g. `accumulate` not 0/1) */
+  PURO_ERR_INPUT = 6   /* debug mode only: input data outside the contract (puro_set_debug) */
 } puro_status;
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -241,6 +243,22 @@ puro_status puro_fp8_gemm_dgrad_pow2(const void* dyq, const float* sdy, const vo
 puro_status puro_fp8_gemm_wgrad_pow2(const void* dytq, const float* sdyt, const void* xtq,
                                      const float* sxt, float* dw, int64_t M, int64_t N, int64_t K,
                                      int accumulate, void* stream);
+
+/* Debug mode: input checks on the device before every quantiser and GEMM.
+ * At level 0 (the default) nothing is checked. At level 1 or more each quantiser and GEMM
+ * entry point, after its host validation, scans its inputs on `stream`, waits for the scan
+ * (the call then synchronises the stream, so debug mode is not for graph capture) and returns
+ * PURO_ERR_INPUT, enqueueing nothing more, when they break the contract above:
+ *   - quantisers: a bf16 NaN or infinity; with the amax/448 rule (not the _pow2 one, which has
+ *     no lower bound) a group of the entry point's shape whose amax is nonzero and below 2^-119;
+ *   - GEMMs: an E4M3 NaN code (0x7F or 0xFF) in either operand, or a scale that is not a
+ *     positive finite float.
+ * The level starts from the environment variable PURO_DEBUG (a positive integer; unset or 0
+ * means off), read the first time it is needed; puro_set_debug overrides it for the process
+ * (negative values mean 0). Checks are serialised by the library; the scans are plain and slow,
+ * meant for finding bad data, not for production runs. */
+void puro_set_debug(int level);
+int puro_debug_level(void);
 
 #ifdef __cplusplus
 }

@@ -233,3 +233,23 @@ def test_probe_library_validation():
         args = list(good)
         args[i] = bad
         assert fn(*args) == 1, (i, bad)
+
+
+def test_debug_level(L):
+    """The debug level is host state: settable, clamped at 0, and read from PURO_DEBUG."""
+    import subprocess
+    import sys
+    before = L.puro_debug_level()
+    try:
+        L.puro_set_debug(2)
+        assert L.puro_debug_level() == 2
+        L.puro_set_debug(-5)
+        assert L.puro_debug_level() == 0
+    finally:
+        L.puro_set_debug(before)
+    code = ("import sys; sys.path.insert(0, %r); from blockwise_fp8_gemm_x128_amd import _lib; "
+            "print(_lib.lib().puro_debug_level())" % ROOT)
+    for env, want in (("3", "3"), ("0", "0"), ("", "0")):
+        out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                             env={**os.environ, "PURO_DEBUG": env}, timeout=120)
+        assert out.stdout.strip() == want, (env, out.stdout, out.stderr)

@@ -10,7 +10,8 @@ recomputes from them:
     first layer's dX of each input width, the first layer's gradient codes of each output
     width, and each linear slot's transposed gradient codes -- bit-exact or within tolerance.
 A buffer routed to the wrong linear or layer shows up as a mismatch here even though it would
-be bitwise identical across the step's launch orders."""
+be bitwise identical across the step's launch orders. Both scale rules: the amax/448 step the
+benchmark times by default and its power-of-two (`--pow2`) twin."""
 import sys
 
 import numpy as np
@@ -43,23 +44,30 @@ def same(gpu: torch.Tensor, ref: np.ndarray, what: str):
     assert bad.size == 0, f"{what}: {len(bad)} byte mismatches, first {bad[:4].tolist()}"
 
 
+def P(stack):
+    """Scale rule of the stack under test (the _pow2 step for the pow2 parameter)."""
+    return stack.test_pow2
+
+
 def within(gpu: np.ndarray, ref: np.ndarray, what: str):
     nbad, worst = gemm_tolerance_violations(gpu, ref)
     assert nbad == 0, f"{what}: {nbad} out of tolerance (worst err/bound {worst:.3g})"
     say("  ", what, "worst err/bound", round(worst, 4))
 
 
-@pytest.fixture(scope="module")
-def stepped():
+@pytest.fixture(scope="module", params=[False, True], ids=["amax448", "pow2"])
+def stepped(request):
     import bench
-    say("stack parity: building", LAYERS, "layers at M =", M)
+    pow2 = request.param
+    say("stack parity: building", LAYERS, "layers at M =", M, "pow2" if pow2 else "")
     main = torch.cuda.Stream()
     with torch.cuda.stream(main):
-        stack = bench.Stack(LAYERS, M)
+        stack = bench.Stack(LAYERS, M, pow2=pow2)
         stack.capture(overlap=False)
         stack.replay()
     torch.cuda.synchronize()
     say("stack parity: step replayed")
+    stack.test_pow2 = pow2
     return stack
 
 
@@ -67,10 +75,10 @@ def test_per_layer_weights_and_transposed_x(stepped, oracle):
     for rec in stepped.linears:
         what = f"layer {rec['layer']} {rec['name']}"
         say("stack parity:", what, "weight and X^T codes")
-        wq, sw = oracle.quant_w_128x128(bf16_np(rec["w"].cpu()))
+        wq, sw = oracle.quant_w_128x128(bf16_np(rec["w"].cpu()), pow2=P(stepped))
         same(rec["wq"], wq, what + " wq")
         same(rec["sw"], sw, what + " sw")
-        xtq, sxt = oracle.quant_transpose(bf16_np(rec["x"].cpu()))
+        xtq, sxt = oracle.quant_transpose(bf16_np(rec["x"].cpu()), pow2=P(stepped))
         same(rec["xtq"], xtq, what + " xtq")
         same(rec["sxt"], sxt, what + " sxt")
 
@@ -79,8 +87,8 @@ def test_per_layer_weight_gradients(stepped, oracle):
     for rec in stepped.linears:
         what = f"layer {rec['layer']} {rec['name']} dW"
         say("stack parity:", what)
-        dytq, sdyt = oracle.quant_transpose(bf16_np(rec["dy"].cpu()))
-        xtq, sxt = oracle.quant_transpose(bf16_np(rec["x"].cpu()))
+        dytq, sdyt = oracle.quant_transpose(bf16_np(rec["dy"].cpu()), pow2=P(stepped))
+        xtq, sxt = oracle.quant_transpose(bf16_np(rec["x"].cpu()), pow2=P(stepped))
         rows = sample_rows(rec["N"], 8, 31 * rec["layer"] + rec["li"])
         ref = oracle.gemm_wgrad(dytq, sdyt, xtq, sxt, rows=rows)
         got = rec["dw"][torch.as_tensor(rows).cuda()].cpu().numpy().astype(np.float64)
@@ -100,8 +108,8 @@ def test_surviving_shared_buffers(stepped, oracle):
     for name, key_y in (("qkv", ("y", M, 4096)), ("gate_up", ("y", M, 12288)),
                         ("down", ("y", M, 2048))):
         rec = _last(stepped, last, name)
-        xq, sx = oracle.quant_act_1x128(bf16_np(rec["x"].cpu()))
-        wq, sw = oracle.quant_w_128x128(bf16_np(rec["w"].cpu()))
+        xq, sx = oracle.quant_act_1x128(bf16_np(rec["x"].cpu()), pow2=P(stepped))
+        wq, sw = oracle.quant_w_128x128(bf16_np(rec["w"].cpu()), pow2=P(stepped))
         say("stack parity: Y of layer", last, name)
         ref = oracle.gemm_fwd(xq, sx, wq, sw, rows=rows)
         within(sh[key_y][rsel].float().cpu().numpy().astype(np.float64), ref,
@@ -113,18 +121,18 @@ def test_surviving_shared_buffers(stepped, oracle):
     for name in ("qkv", "o", "gate_up", "down"):
         rec = _last(stepped, first, name)
         dy = bf16_np(rec["dy"].cpu())
-        dytq, sdyt = oracle.quant_transpose(dy)
+        dytq, sdyt = oracle.quant_transpose(dy, pow2=P(stepped))
         same(sh[("dytq", rec["li"])], dytq, f"dytq slot {name} (layer {first})")
         same(sh[("sdyt", rec["li"])], sdyt, f"sdyt slot {name} (layer {first})")
         if name == "down":
             continue  # its dY codes are overwritten by o's (same width)
-        dyq, sdy = oracle.quant_act_1x128(dy)
+        dyq, sdy = oracle.quant_act_1x128(dy, pow2=P(stepped))
         same(sh[("dyq", M, rec["N"])], dyq, f"dyq layer {first} {name}")
         same(sh[("sdy", M, rec["N"])], sdy, f"sdy layer {first} {name}")
     for name in ("qkv", "down"):  # last writers of dX for K = 2048 and K = 6144
         rec = _last(stepped, first, name)
-        dyq, sdy = oracle.quant_act_1x128(bf16_np(rec["dy"].cpu()))
-        wq, sw = oracle.quant_w_128x128(bf16_np(rec["w"].cpu()))
+        dyq, sdy = oracle.quant_act_1x128(bf16_np(rec["dy"].cpu()), pow2=P(stepped))
+        wq, sw = oracle.quant_w_128x128(bf16_np(rec["w"].cpu()), pow2=P(stepped))
         say("stack parity: dX of layer", first, name)
         ref = oracle.gemm_dgrad(dyq, sdy, wq, sw, rows=rows)
         within(sh[("dx", M, rec["K"])][rsel].float().cpu().numpy().astype(np.float64), ref,

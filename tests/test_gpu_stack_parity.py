@@ -10,8 +10,9 @@ recomputes from them:
     first layer's dX of each input width, the first layer's gradient codes of each output
     width, and each linear slot's transposed gradient codes -- bit-exact or within tolerance.
 A buffer routed to the wrong linear or layer shows up as a mismatch here even though it would
-be bitwise identical across the step's launch orders. Both scale rules: the amax/448 step the
-benchmark times by default and its power-of-two (`--pow2`) twin."""
+be bitwise identical across the step's launch orders. Three steps: the amax/448 step the
+benchmark times by default, its power-of-two (`--pow2`) twin, and the unfused step
+(`--unfused`: separate 1x128 and transposed quantisers instead of the two-orientation one)."""
 import sys
 
 import numpy as np
@@ -55,14 +56,16 @@ def within(gpu: np.ndarray, ref: np.ndarray, what: str):
     say("  ", what, "worst err/bound", round(worst, 4))
 
 
-@pytest.fixture(scope="module", params=[False, True], ids=["amax448", "pow2"])
+@pytest.fixture(scope="module", params=[(True, False), (True, True), (False, False)],
+                ids=["amax448", "pow2", "unfused"])
 def stepped(request):
     import bench
-    pow2 = request.param
-    say("stack parity: building", LAYERS, "layers at M =", M, "pow2" if pow2 else "")
+    fused, pow2 = request.param
+    say("stack parity: building", LAYERS, "layers at M =", M, "pow2" if pow2 else "",
+        "" if fused else "unfused")
     main = torch.cuda.Stream()
     with torch.cuda.stream(main):
-        stack = bench.Stack(LAYERS, M, pow2=pow2)
+        stack = bench.Stack(LAYERS, M, fused=fused, pow2=pow2)
         stack.capture(overlap=False)
         stack.replay()
     torch.cuda.synchronize()
@@ -78,6 +81,8 @@ def test_per_layer_weights_and_transposed_x(stepped, oracle):
         wq, sw = oracle.quant_w_128x128(bf16_np(rec["w"].cpu()), pow2=P(stepped))
         same(rec["wq"], wq, what + " wq")
         same(rec["sw"], sw, what + " sw")
+        if "xtq" not in rec:
+            continue  # unfused step: X's transposed copy is a shared buffer (checked below)
         xtq, sxt = oracle.quant_transpose(bf16_np(rec["x"].cpu()), pow2=P(stepped))
         same(rec["xtq"], xtq, what + " xtq")
         same(rec["sxt"], sxt, what + " sxt")
@@ -129,6 +134,12 @@ def test_surviving_shared_buffers(stepped, oracle):
         dyq, sdy = oracle.quant_act_1x128(dy, pow2=P(stepped))
         same(sh[("dyq", M, rec["N"])], dyq, f"dyq layer {first} {name}")
         same(sh[("sdy", M, rec["N"])], sdy, f"sdy layer {first} {name}")
+    for name in ("qkv", "down"):  # last writers of X's shared transposed copy (unfused step)
+        rec = _last(stepped, first, name)
+        if ("xtq", M, rec["K"]) in sh:
+            xtq, sxt = oracle.quant_transpose(bf16_np(rec["x"].cpu()), pow2=P(stepped))
+            same(sh[("xtq", M, rec["K"])], xtq, f"xtq layer {first} {name}")
+            same(sh[("sxt", M, rec["K"])], sxt, f"sxt layer {first} {name}")
     for name in ("qkv", "down"):  # last writers of dX for K = 2048 and K = 6144
         rec = _last(stepped, first, name)
         dyq, sdy = oracle.quant_act_1x128(bf16_np(rec["dy"].cpu()), pow2=P(stepped))

@@ -76,11 +76,15 @@ enum Mode : int { kFwd = 0, kDgrad = 1, kWgrad = 2 };
 
 constexpr int kChunk = 128;       // reduction chunk = quantisation group
 constexpr int kSlab = 128 * 128;  // bytes of one 128-row x 128-byte staged slab
-// Tile-rows per band of the block order: 4 for the forward and data-gradient 256x256 tiles,
-// 8 for the others (measured on the linear-stack step).
+// Tile-rows per band of the block order, for an output `tiles_j` tiles wide: for the forward
+// and data-gradient 256x256 tiles 2 up to 24 tile columns and 4 beyond, 8 for the others
+// (measured on the linear-stack step, same box, alternated: from 4 to 2 the 16-column qkv
+// forward went 62.8 -> 61.1 us and the 24-column down data gradient 91.3 -> 89.7 us, while the
+// 48-column gate_up forward went 169.0 -> 169.8 us; the 8-column shapes did not move).
 template <int kMode, int BM>
-constexpr int group_rows() {
-  return (kMode != kWgrad && BM == 256) ? 4 : 8;
+__device__ __forceinline__ int64_t band_rows(int64_t tiles_j) {
+  if constexpr (kMode != kWgrad && BM == 256) return tiles_j <= 24 ? 2 : 4;
+  return 8;
 }
 
 template <int kMode, int BM_, int BN_, int WAVES_M_, int WAVES_N_, bool kPow2_ = false>
@@ -89,7 +93,6 @@ struct Cfg {
   static constexpr bool kPow2 = kPow2_;  // power-of-two scales, applied by the matrix cores
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
-  static constexpr int kGroupRows = group_rows<kMode, BM_>();
   static constexpr int kWaves = WAVES_M * WAVES_N;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -622,7 +625,7 @@ __device__ __forceinline__ void compute_chunk_pow2(const lds_u8* stage, float sb
 
 // Tile origin of this block. Workgroups are dealt round-robin to the 8 XCDs, so the block id is
 // first remapped so that consecutive tiles run on one XCD; tiles are then walked in bands of
-// kGroupRows tile-rows, column by column.
+// band_rows tile-rows, column by column.
 template <class C>
 __device__ __forceinline__ void tile_origin(int64_t I, int64_t J, int64_t& i0, int64_t& j0) {
   const int64_t tiles_i = (I + C::BM - 1) / C::BM;
@@ -630,11 +633,12 @@ __device__ __forceinline__ void tile_origin(int64_t I, int64_t J, int64_t& i0, i
   const int64_t nwg = tiles_i * tiles_j;
   int64_t b = blockIdx.x;
   if ((nwg & 7) == 0) b = (b & 7) * (nwg >> 3) + (b >> 3);
-  const int64_t band = b / (C::kGroupRows * tiles_j);
-  const int64_t band_rows = imin64(C::kGroupRows, tiles_i - band * C::kGroupRows);
-  const int64_t local = b - band * C::kGroupRows * tiles_j;
-  const int64_t ti = band * C::kGroupRows + local % band_rows;
-  const int64_t tj = local / band_rows;
+  const int64_t grp = band_rows<C::mode, C::BM>(tiles_j);
+  const int64_t band = b / (grp * tiles_j);
+  const int64_t rows = imin64(grp, tiles_i - band * grp);
+  const int64_t local = b - band * grp * tiles_j;
+  const int64_t ti = band * grp + local % rows;
+  const int64_t tj = local / rows;
   i0 = uniform64(ti * C::BM);
   j0 = uniform64(tj * C::BN);
 }

@@ -349,25 +349,28 @@ def test_pow2_gemm_reads_only_scale_exponents(puro):
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
 
 
-# Every element of one full-size output per big-tile kernel: the 256x256 forward (qkv at
-# M = 4096: one round of 256 tiles), the 256x256 data gradient (down at M = 4096: 384 tiles),
-# and the weight-gradient tiles 256x256 (4096 x 4096), 192x256 (12288 x 2048) and 256x192
-# (2048 x 6144) over a 512-token reduction.
-def test_big_tiles_full_output_fwd(puro, oracle):
+# Every element of one full-size output per big-tile kernel, for both scale rules: the 256x256
+# forward (qkv at M = 4096: one round of 256 tiles), the 256x256 data gradient (down at
+# M = 4096: 384 tiles), and the weight-gradient tiles 256x256 (4096 x 4096), 192x256
+# (12288 x 2048) and 256x192 (2048 x 6144) over a 512-token reduction.
+@pytest.mark.parametrize("p2", [False, True], ids=["amax448", "pow2"])
+def test_big_tiles_full_output_fwd(puro, oracle, p2):
     name, K, N = synth.LINEARS[0]
     x, w, _ = synth.linear_inputs(1, 0, 4096, K, N)
-    run_fwd(puro, oracle, x, w, what=f"{name} fwd M=4096 every element")
+    run_fwd(puro, oracle, x, w, what=f"{name} fwd M=4096 every element", pow2=p2)
 
 
-def test_big_tiles_full_output_dgrad(puro, oracle):
+@pytest.mark.parametrize("p2", [False, True], ids=["amax448", "pow2"])
+def test_big_tiles_full_output_dgrad(puro, oracle, p2):
     name, K, N = synth.LINEARS[3]
     _, w, dy = synth.linear_inputs(1, 3, 4096, K, N)
-    run_dgrad(puro, oracle, dy, w, what=f"{name} dgrad M=4096 every element")
+    run_dgrad(puro, oracle, dy, w, what=f"{name} dgrad M=4096 every element", pow2=p2)
 
 
+@pytest.mark.parametrize("p2", [False, True], ids=["amax448", "pow2"])
 @pytest.mark.parametrize("N,K", [(4096, 4096), (12288, 2048), (2048, 6144)])
-def test_big_tiles_full_output_wgrad(puro, oracle, N, K):
+def test_big_tiles_full_output_wgrad(puro, oracle, N, K, p2):
     M = 512
     x = synth.randn_bf16((M, K), 1.0, 141 + K)
     dy = synth.randn_bf16((M, N), 1e-3, 142 + N)
-    run_wgrad(puro, oracle, dy, x, what=f"wgrad {N}x{K} (M={M}) every element")
+    run_wgrad(puro, oracle, dy, x, what=f"wgrad {N}x{K} (M={M}) every element", pow2=p2)

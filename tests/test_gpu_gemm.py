@@ -351,8 +351,9 @@ def test_pow2_gemm_reads_only_scale_exponents(puro):
 
 # Every element of one full-size output per big-tile kernel, for both scale rules: the 256x256
 # forward (qkv at M = 4096: one round of 256 tiles), the 256x256 data gradient (down at
-# M = 4096: 384 tiles), and the weight-gradient tiles 256x256 (4096 x 4096), 192x256
-# (12288 x 2048) and 256x192 (2048 x 6144) over a 512-token reduction.
+# M = 4096: 384 tiles), and every weight-gradient tile shape the model uses: 256x256
+# (4096 x 4096), 192x256 (12288 x 2048), 256x192 (2048 x 6144), the 4-wave 128x128 (qkv,
+# 4096 x 2048) and the split-reduction 128x128 (o, 2048 x 2048), over a 512-token reduction.
 @pytest.mark.parametrize("p2", [False, True], ids=["amax448", "pow2"])
 def test_big_tiles_full_output_fwd(puro, oracle, p2):
     name, K, N = synth.LINEARS[0]
@@ -368,7 +369,8 @@ def test_big_tiles_full_output_dgrad(puro, oracle, p2):
 
 
 @pytest.mark.parametrize("p2", [False, True], ids=["amax448", "pow2"])
-@pytest.mark.parametrize("N,K", [(4096, 4096), (12288, 2048), (2048, 6144)])
+@pytest.mark.parametrize("N,K", [(4096, 4096), (12288, 2048), (2048, 6144), (4096, 2048),
+                                 (2048, 2048)])
 def test_big_tiles_full_output_wgrad(puro, oracle, N, K, p2):
     M = 512
     x = synth.randn_bf16((M, K), 1.0, 141 + K)
